@@ -1,0 +1,304 @@
+"""CPU oracle for the TQ4 paged KV codec and attention over it.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the GPU library and
+its Python binding never do, and this package never imports them.
+
+The arithmetic lives in ``tq4_oracle.c`` (plain scalar C, fp64 attention, the
+encoder in fp32 as the readings there fix it); this module only builds that
+file with gcc, loads it with ctypes and marshals numpy arrays.
+
+Sources, by page and section:
+  * "Fitting a 27B-Parameter LLM into 24 GiB of Laptop Memory"
+    (simpleprog.com), section "KVExec: Fused Reconstruction with
+    Layer-Scoped Lifetime" -- record format (32 U32 words of eight indices,
+    one FP16 norm) and the decode steps (page IDs, centroid lookup, inverse
+    Hadamard rotation, norm restore, scaled dot-product attention).
+  * same page, section "The Memory Budget Equation" -- 4 KV heads of
+    dimension 256, 16 full-attention layers, 16,640 B per position vs
+    65,536 B in FP16, 3,640 MiB vs 14,336 MiB at 229,376 positions, and
+    768 MiB of BF16 K/V for one layer at 192K positions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "tq4_oracle.c")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_PATH = os.path.join(BUILD_DIR, "libtq4oracle.so")
+
+DIM = 256
+WORDS = 32
+LEVELS = 16
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no contraction)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-ffp-contract=off",
+               "-fno-fast-math", "-fPIC", "-shared", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    c_f32p, c_f64p = P(ctypes.c_float), P(ctypes.c_double)
+    c_u32p, c_u16p, c_i32p = P(ctypes.c_uint32), P(ctypes.c_uint16), P(ctypes.c_int32)
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    lib.tq4o_lloyd_max16.argtypes = [c_f64p, c_f64p, c_f64p, ctypes.c_int]
+    lib.tq4o_lloyd_max16.restype = ctypes.c_int
+    lib.tq4o_codebook.argtypes = [c_f32p, c_f32p]
+    lib.tq4o_f32_to_f16_array.argtypes = [c_f32p, c_u16p, i64]
+    lib.tq4o_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.tq4o_f16_to_f64.restype = ctypes.c_double
+    lib.tq4o_encode_many.argtypes = [c_f32p, i64, c_u32p, c_u16p]
+    lib.tq4o_decode_many.argtypes = [c_u32p, c_u16p, i64, c_f64p]
+    lib.tq4o_fwht_f32_many.argtypes = [c_f32p, i64]
+    lib.tq4o_fwht_f64_many.argtypes = [c_f64p, i64]
+    lib.tq4o_encode_to_pool.argtypes = [c_u32p, c_u16p, i32, i32, i32, c_f32p, c_i32p, i32]
+    lib.tq4o_encode_to_pool.restype = ctypes.c_int
+    lib.tq4o_attention.argtypes = [c_u32p, c_u16p, c_u32p, c_u16p, i32, i32, i32,
+                                   c_f64p, i32, i32, c_i32p, i32, c_i32p, c_i32p,
+                                   ctypes.c_double, i32, i32, c_f64p]
+    lib.tq4o_attention.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# --------------------------------------------------------------------------
+# Constants
+# --------------------------------------------------------------------------
+
+def lloyd_max16(max_iter: int = 1_000_000):
+    """Lloyd-Max levels/boundaries for N(0,1), 16 levels, in fp64.
+
+    Returns (levels[16], bounds[15], distortion, iterations)."""
+    lib = _load()
+    lev = np.zeros(LEVELS, np.float64)
+    bnd = np.zeros(LEVELS - 1, np.float64)
+    dist = ctypes.c_double(0.0)
+    it = lib.tq4o_lloyd_max16(_ptr(lev, ctypes.c_double), _ptr(bnd, ctypes.c_double),
+                              ctypes.byref(dist), max_iter)
+    return lev, bnd, dist.value, it
+
+
+def codebook():
+    """(centroids fp32[16] ascending, thresholds fp32[15])."""
+    lib = _load()
+    c = np.zeros(LEVELS, np.float32)
+    b = np.zeros(LEVELS - 1, np.float32)
+    lib.tq4o_codebook(_ptr(c, ctypes.c_float), _ptr(b, ctypes.c_float))
+    return c, b
+
+
+# --------------------------------------------------------------------------
+# Elementwise helpers
+# --------------------------------------------------------------------------
+
+def f32_to_f16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.shape, np.uint16)
+    _load().tq4o_f32_to_f16_array(_ptr(x.reshape(-1), ctypes.c_float),
+                                  _ptr(out.reshape(-1), ctypes.c_uint16), x.size)
+    return out
+
+
+def f16_bits_to_f64(h) -> np.ndarray:
+    lib = _load()
+    h = np.asarray(h, dtype=np.uint16)
+    return np.array([lib.tq4o_f16_to_f64(int(v)) for v in h.reshape(-1)],
+                    np.float64).reshape(h.shape)
+
+
+def fwht_f32(x) -> np.ndarray:
+    y = np.array(x, dtype=np.float32, copy=True, order="C").reshape(-1, DIM)
+    _load().tq4o_fwht_f32_many(_ptr(y, ctypes.c_float), y.shape[0])
+    return y.reshape(np.shape(x))
+
+
+def fwht_f64(x) -> np.ndarray:
+    y = np.array(x, dtype=np.float64, copy=True, order="C").reshape(-1, DIM)
+    _load().tq4o_fwht_f64_many(_ptr(y, ctypes.c_double), y.shape[0])
+    return y.reshape(np.shape(x))
+
+
+# --------------------------------------------------------------------------
+# Codec
+# --------------------------------------------------------------------------
+
+def encode(x):
+    """Encode fp32 vectors [..., 256] -> (words uint32 [..., 32], norms uint16 [...])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape[-1] == DIM
+    lead = x.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    words = np.zeros((n, WORDS), np.uint32)
+    norms = np.zeros((n,), np.uint16)
+    _load().tq4o_encode_many(_ptr(x.reshape(n, DIM), ctypes.c_float), n,
+                             _ptr(words, ctypes.c_uint32), _ptr(norms, ctypes.c_uint16))
+    return words.reshape(*lead, WORDS), norms.reshape(lead)
+
+
+def decode(words, norms) -> np.ndarray:
+    """Exact fp64 reconstruction of records (words [..., 32], norms [...])."""
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    norms = np.ascontiguousarray(norms, dtype=np.uint16)
+    lead = norms.shape
+    n = int(np.prod(lead)) if lead else 1
+    out = np.zeros((n, DIM), np.float64)
+    _load().tq4o_decode_many(_ptr(words.reshape(n, WORDS), ctypes.c_uint32),
+                             _ptr(norms.reshape(n), ctypes.c_uint16), n,
+                             _ptr(out, ctypes.c_double))
+    return out.reshape(*lead, DIM)
+
+
+def unpack(words) -> np.ndarray:
+    """Indices [..., 256] of packed words [..., 32] (dim 8k+j in bits 4j.. of word k)."""
+    w = np.asarray(words, dtype=np.uint32)
+    shifts = (4 * np.arange(8, dtype=np.uint32))
+    idx = (w[..., :, None] >> shifts) & np.uint32(0xF)
+    return idx.reshape(*w.shape[:-1], DIM).astype(np.uint8)
+
+
+def pack(idx) -> np.ndarray:
+    idx = np.asarray(idx, dtype=np.uint32).reshape(*np.shape(idx)[:-1], WORDS, 8)
+    shifts = (4 * np.arange(8, dtype=np.uint32))
+    return np.bitwise_or.reduce(idx << shifts, axis=-1).astype(np.uint32)
+
+
+# --------------------------------------------------------------------------
+# Paged pools
+# --------------------------------------------------------------------------
+
+@dataclass
+class Pool:
+    """One layer's TQ4 page pool (host arrays).
+
+    words: uint32 [num_pages][n_kv][P][32]; norms: fp16 bits [num_pages][n_kv][P]."""
+    k_words: np.ndarray
+    k_norms: np.ndarray
+    v_words: np.ndarray
+    v_norms: np.ndarray
+
+    @property
+    def num_pages(self):
+        return self.k_words.shape[0]
+
+    @property
+    def n_kv(self):
+        return self.k_words.shape[1]
+
+    @property
+    def page_size(self):
+        return self.k_words.shape[2]
+
+    @staticmethod
+    def empty(num_pages: int, n_kv: int, page_size: int) -> "Pool":
+        shp = (num_pages, n_kv, page_size)
+        return Pool(np.zeros(shp + (WORDS,), np.uint32), np.zeros(shp, np.uint16),
+                    np.zeros(shp + (WORDS,), np.uint32), np.zeros(shp, np.uint16))
+
+
+def encode_to_pool(pool: Pool, k_src, v_src, slots) -> None:
+    """Encode source K and V [n_tokens][n_kv][256] (fp32) into records at slots."""
+    lib = _load()
+    slots = np.ascontiguousarray(slots, dtype=np.int32)
+    for src, words, norms in ((k_src, pool.k_words, pool.k_norms),
+                              (v_src, pool.v_words, pool.v_norms)):
+        if src is None:
+            continue
+        src = np.ascontiguousarray(src, dtype=np.float32)
+        assert src.shape == (slots.shape[0], pool.n_kv, DIM)
+        rc = lib.tq4o_encode_to_pool(_ptr(words, ctypes.c_uint32), _ptr(norms, ctypes.c_uint16),
+                                     pool.num_pages, pool.n_kv, pool.page_size,
+                                     _ptr(src, ctypes.c_float), _ptr(slots, ctypes.c_int32),
+                                     slots.shape[0])
+        if rc != 0:
+            raise ValueError("slot outside the pool")
+
+
+def attention(pool: Pool, q, page_table, row_table, row_len, scale: float,
+              heads: tuple | None = None) -> np.ndarray:
+    """fp64 softmax attention over TQ4 pages.
+
+    q: [n_rows][n_q][256] (values exactly representable in fp64, e.g. bf16 inputs);
+    page_table: int32 [n_tables][stride]; row_table[r]: which table row query
+    row r reads; row_len[r]: how many leading positions it attends.
+    Returns fp64 [n_rows][n_q][256]; heads outside `heads` = (h0, h1) stay 0."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    n_rows, n_q, d = q.shape
+    assert d == DIM and n_q % pool.n_kv == 0
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    if pt.ndim == 1:
+        pt = pt[None, :]
+    rt = np.ascontiguousarray(row_table, dtype=np.int32)
+    rl = np.ascontiguousarray(row_len, dtype=np.int32)
+    assert rt.shape == (n_rows,) and rl.shape == (n_rows,)
+    h0, h1 = heads if heads is not None else (0, n_q)
+    out = np.zeros((n_rows, n_q, DIM), np.float64)
+    rc = _load().tq4o_attention(
+        _ptr(pool.k_words, ctypes.c_uint32), _ptr(pool.k_norms, ctypes.c_uint16),
+        _ptr(pool.v_words, ctypes.c_uint32), _ptr(pool.v_norms, ctypes.c_uint16),
+        pool.num_pages, pool.n_kv, pool.page_size, _ptr(q, ctypes.c_double), n_q, n_rows,
+        _ptr(pt, ctypes.c_int32), pt.shape[1], _ptr(rt, ctypes.c_int32), _ptr(rl, ctypes.c_int32),
+        float(scale), h0, h1, _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle attention failed ({rc})")
+    return out
+
+
+def attn_decode(pool: Pool, q, page_table, seq_lens, scale: float, heads=None) -> np.ndarray:
+    """Single-query decode for each request b: q[b] attends positions 0..seq_lens[b]-1."""
+    q = np.asarray(q)
+    batch = q.shape[0]
+    return attention(pool, q, page_table, np.arange(batch, dtype=np.int32),
+                     np.asarray(seq_lens, np.int32), scale, heads)
+
+
+def attn_prefill_rows(pool: Pool, q_rows, rows, page_table_row, prior_len: int, scale: float,
+                      heads=None) -> np.ndarray:
+    """Chunk rows t (absolute position prior_len + t) attend positions 0..prior_len + t."""
+    rows = np.asarray(rows, np.int32)
+    return attention(pool, q_rows, np.asarray(page_table_row, np.int32)[None, :],
+                     np.zeros(len(rows), np.int32), prior_len + rows + 1, scale, heads)
+
+
+# --------------------------------------------------------------------------
+# Closed-form sizes (section "The Memory Budget Equation")
+# --------------------------------------------------------------------------
+
+def bytes_per_vector() -> int:
+    """32 U32 words + one FP16 norm."""
+    return WORDS * 4 + 2
+
+
+def bytes_per_position(n_layers: int = 16, n_kv: int = 4) -> int:
+    """TQ4 bytes one cached position occupies across all full-attention layers (K and V)."""
+    return n_layers * n_kv * 2 * bytes_per_vector()
+
+
+def fp16_bytes_per_position(n_layers: int = 16, n_kv: int = 4, dim: int = DIM) -> int:
+    return n_layers * n_kv * 2 * dim * 2

@@ -1,0 +1,152 @@
+"""Pins for the oracle's attention half: closed forms, a 50-digit brute force on
+tiny inputs, GQA head mapping, and page-placement invariance."""
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+import scipy.linalg
+
+import synth
+
+
+def _rand_pool(oracle_mod, num_pages, n_kv, P, n_tokens, seed):
+    rng = np.random.default_rng(seed)
+    pool = oracle_mod.Pool.empty(num_pages, n_kv, P)
+    k = rng.standard_normal((n_tokens, n_kv, 256)).astype(np.float32)
+    v = rng.standard_normal((n_tokens, n_kv, 256)).astype(np.float32)
+    table = rng.permutation(num_pages)[: -(-n_tokens // P)].astype(np.int32)
+    slots = (table[np.arange(n_tokens) // P] * P + np.arange(n_tokens) % P).astype(np.int32)
+    oracle_mod.encode_to_pool(pool, k, v, slots)
+    return pool, table
+
+
+def _bf16_q(rows, n_q, seed, scale=1.0):
+    return synth.bf16_round(np.random.default_rng(seed).standard_normal((rows, n_q, 256)) * scale)
+
+
+def _records(pool, table, n_tokens, g, which):
+    P = pool.page_size
+    words = pool.k_words if which == "k" else pool.v_words
+    norms = pool.k_norms if which == "k" else pool.v_norms
+    pages, offs = table[np.arange(n_tokens) // P], np.arange(n_tokens) % P
+    return words[pages, g, offs], norms[pages, g, offs]
+
+
+def test_single_position_returns_its_value(oracle_mod):
+    pool, table = _rand_pool(oracle_mod, 4, 2, 64, 1, 11)
+    q = _bf16_q(1, 6, 12)
+    out = oracle_mod.attn_decode(pool, q, table[None], [1], 1 / 16)
+    for g in range(2):
+        w, n = _records(pool, table, 1, g, "v")
+        vh = oracle_mod.decode(w, n)[0]
+        for h in range(3 * g, 3 * g + 3):
+            np.testing.assert_array_equal(out[0, h], vh)
+
+
+def test_two_positions_closed_form(oracle_mod):
+    pool, table = _rand_pool(oracle_mod, 4, 1, 64, 2, 13)
+    q = _bf16_q(1, 2, 14)
+    out = oracle_mod.attn_decode(pool, q, table[None], [2], 1 / 16)
+    kw, kn = _records(pool, table, 2, 0, "k")
+    vw, vn = _records(pool, table, 2, 0, "v")
+    kh, vh = oracle_mod.decode(kw, kn), oracle_mod.decode(vw, vn)
+    for h in range(2):
+        s0, s1 = (kh @ q[0, h].astype(np.float64)) / 16
+        w0 = 1 / (1 + np.exp(s1 - s0))
+        ref = w0 * vh[0] + (1 - w0) * vh[1]
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_zero_query_and_identical_keys_give_mean_of_values(oracle_mod):
+    n = 150
+    pool, table = _rand_pool(oracle_mod, 8, 1, 64, n, 15)
+    vw, vn = _records(pool, table, n, 0, "v")
+    mean_v = oracle_mod.decode(vw, vn).mean(axis=0)
+    out = oracle_mod.attn_decode(pool, np.zeros((1, 1, 256)), table[None], [n], 1 / 16)
+    np.testing.assert_allclose(out[0, 0], mean_v, rtol=1e-12, atol=1e-12)
+    # identical keys: copy one K record over every position
+    P = pool.page_size
+    pages, offs = table[np.arange(n) // P], np.arange(n) % P
+    pool.k_words[pages, 0, offs] = pool.k_words[pages[0], 0, offs[0]]
+    pool.k_norms[pages, 0, offs] = pool.k_norms[pages[0], 0, offs[0]]
+    out = oracle_mod.attn_decode(pool, _bf16_q(1, 1, 16), table[None], [n], 1 / 16)
+    np.testing.assert_allclose(out[0, 0], mean_v, rtol=1e-12, atol=1e-12)
+
+
+def _mpf(fr):
+    return mpmath.mpf(fr.numerator) / fr.denominator
+
+
+def test_brute_force_50_digits(oracle_mod):
+    """Dense Hadamard decode in exact rationals and softmax in 50-digit arithmetic."""
+    mpmath.mp.dps = 50
+    c, _ = oracle_mod.codebook()
+    cF = [Fraction(float(v)) for v in c]
+    H = scipy.linalg.hadamard(256)
+    for L, seed in [(1, 21), (3, 22), (8, 23)]:
+        pool, table = _rand_pool(oracle_mod, 3, 2, 64, L, seed)
+        q = _bf16_q(1, 4, seed + 100, scale=4.0)      # peaked softmax
+        out = oracle_mod.attn_decode(pool, q, table[None], [L], 1 / 16)
+        for g in range(2):
+            dec = {}
+            for which in ("k", "v"):
+                w, n = _records(pool, table, L, g, which)
+                idx = oracle_mod.unpack(w)
+                vecs = []
+                for j in range(L):
+                    nj = Fraction(float(np.uint16(n[j]).view(np.float16)))
+                    ys = np.array([cF[i] for i in idx[j]], dtype=object)
+                    vecs.append([nj * sum(int(H[d, t]) * ys[t] for t in range(256)) / 16
+                                 for d in range(256)])
+                dec[which] = vecs
+            for h in (2 * g, 2 * g + 1):
+                qh = [Fraction(float(v)) for v in q[0, h]]
+                s = [_mpf(sum(a * b for a, b in zip(qh, dec["k"][j]))) / 16 for j in range(L)]
+                mx = max(s)
+                e = [mpmath.exp(x - mx) for x in s]
+                tot = sum(e)
+                for d in (0, 5, 128, 255):
+                    ref = sum(e[j] * _mpf(dec["v"][j][d]) for j in range(L)) / tot
+                    assert abs(float(ref) - out[0, h, d]) <= 1e-12 * max(1.0, abs(float(ref)))
+
+
+def test_gqa_heads_read_their_group(oracle_mod):
+    """With 12 query heads over 4 KV heads, head h reads KV head h // 3."""
+    n = 70
+    pool, table = _rand_pool(oracle_mod, 4, 4, 64, n, 31)
+    q = _bf16_q(1, 12, 32)
+    out = oracle_mod.attn_decode(pool, q, table[None], [n], 1 / 16)
+    for h in range(12):
+        g = h // 3
+        single = oracle_mod.Pool(pool.k_words[:, g:g + 1].copy(), pool.k_norms[:, g:g + 1].copy(),
+                                 pool.v_words[:, g:g + 1].copy(), pool.v_norms[:, g:g + 1].copy())
+        ref = oracle_mod.attn_decode(single, q[:, h:h + 1], table[None], [n], 1 / 16)
+        np.testing.assert_array_equal(out[0, h], ref[0, 0])
+
+
+def test_physical_page_permutation_invariance(oracle_mod):
+    n = 300
+    pool, table = _rand_pool(oracle_mod, 8, 2, 64, n, 41)
+    q = _bf16_q(2, 4, 42)
+    tables = np.stack([table, table])
+    out = oracle_mod.attn_decode(pool, q, tables, [n, n - 77], 1 / 16)
+    perm = np.random.default_rng(43).permutation(8)
+    inv = np.argsort(perm)
+    moved = oracle_mod.Pool(pool.k_words[inv].copy(), pool.k_norms[inv].copy(),
+                            pool.v_words[inv].copy(), pool.v_norms[inv].copy())
+    out2 = oracle_mod.attn_decode(moved, q, perm[tables].astype(np.int32), [n, n - 77], 1 / 16)
+    np.testing.assert_array_equal(out, out2)
+
+
+def test_prefill_rows_are_causal(oracle_mod):
+    """Row t of a chunk over P0 cached positions sees exactly P0 + t + 1 keys."""
+    prior, chunk = 100, 28
+    pool, table = _rand_pool(oracle_mod, 4, 1, 64, prior + chunk, 51)
+    q = _bf16_q(chunk, 2, 52)
+    rows = np.array([0, 5, 27])
+    out = oracle_mod.attn_prefill_rows(pool, q[rows], rows, table, prior, 1 / 16)
+    for r, t in enumerate(rows):
+        ref = oracle_mod.attn_decode(pool, q[t:t + 1], table[None], [prior + t + 1], 1 / 16)
+        np.testing.assert_array_equal(out[r], ref[0])
+        shorter = oracle_mod.attn_decode(pool, q[t:t + 1], table[None], [prior + t], 1 / 16)
+        assert np.any(out[r] != shorter[0])
