@@ -1,0 +1,156 @@
+"""TQ4 paged-KV attention for AMD Instinct MI355X (gfx950).
+
+Python face of the C ABI in include/tq4.h (functions keep the C names).  It
+marshals torch tensors into pointers and the current HIP stream; the work runs
+in the library's HIP kernels.
+
+Pool layout (one layer): k_words / v_words int32 bit patterns of uint32 words
+[num_pages][n_kv][page_size][32]; k_norms / v_norms int16 bit patterns of fp16
+[num_pages][n_kv][page_size].
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from ._binding import (TQ4_BF16, TQ4_F16, TQ4_F32, Tq4Error, check, header_functions,
+                       load_library, tq4_layer_pool)
+
+__all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_encode_pages",
+           "tq4_attn_decode_workspace_size", "tq4_attn_decode", "tq4_attn_prefill_workspace_size",
+           "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library"]
+
+HEAD_DIM = 256
+WORDS = 32
+
+
+@dataclass
+class Tq4LayerPool:
+    k_words: torch.Tensor
+    v_words: torch.Tensor
+    k_norms: torch.Tensor
+    v_norms: torch.Tensor
+
+    @staticmethod
+    def empty(num_pages: int, n_kv: int, page_size: int, device="cuda") -> "Tq4LayerPool":
+        shp = (num_pages, n_kv, page_size)
+        return Tq4LayerPool(torch.zeros(shp + (WORDS,), dtype=torch.int32, device=device),
+                            torch.zeros(shp + (WORDS,), dtype=torch.int32, device=device),
+                            torch.zeros(shp, dtype=torch.int16, device=device),
+                            torch.zeros(shp, dtype=torch.int16, device=device))
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_words.shape[0]
+
+    @property
+    def n_kv(self) -> int:
+        return self.k_words.shape[1]
+
+    @property
+    def page_size(self) -> int:
+        return self.k_words.shape[2]
+
+    def struct(self) -> tq4_layer_pool:
+        for t in (self.k_words, self.v_words, self.k_norms, self.v_norms):
+            if not t.is_contiguous():
+                raise ValueError("pool tensors must be contiguous")
+        return tq4_layer_pool(self.k_words.data_ptr(), self.v_words.data_ptr(),
+                              self.k_norms.data_ptr(), self.v_norms.data_ptr(),
+                              self.num_pages, self.page_size, self.n_kv, HEAD_DIM)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return {torch.float32: TQ4_F32, torch.bfloat16: TQ4_BF16, torch.float16: TQ4_F16}.get(t.dtype, 99)
+
+
+def tq4_abi_version() -> int:
+    return load_library().tq4_abi_version()
+
+
+def tq4_codebook():
+    """(centroids[16], thresholds[15]) as Python floats (host)."""
+    c = (ctypes.c_float * 16)()
+    b = (ctypes.c_float * 15)()
+    check(load_library().tq4_codebook(c, b))
+    return list(c), list(b)
+
+
+def tq4_encode_pages(pool: Tq4LayerPool, k, v, slots: torch.Tensor, stream=None) -> None:
+    """Encode [n_tokens][n_kv][256] fp32/bf16 K and/or V into the records at slots (int32)."""
+    src = k if k is not None else v
+    if src is None:
+        raise ValueError("need k or v")
+    for t in (k, v):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("sources must be contiguous")
+    n_tokens = int(slots.shape[0])
+    ps = pool.struct()
+    check(load_library().tq4_encode_pages(ctypes.byref(ps), _ptr(k), _ptr(v), _dtype_code(src),
+                                          _ptr(slots), n_tokens, _stream(stream)))
+
+
+def tq4_attn_decode_workspace_size(batch: int, max_seq_len: int, n_q_heads: int, n_kv_heads: int,
+                                   page_size: int) -> int:
+    return int(load_library().tq4_attn_decode_workspace_size(batch, max_seq_len, n_q_heads,
+                                                              n_kv_heads, page_size))
+
+
+def tq4_attn_prefill_workspace_size(prior_len: int, chunk_len: int, n_q_heads: int, n_kv_heads: int,
+                                    page_size: int) -> int:
+    return int(load_library().tq4_attn_prefill_workspace_size(prior_len, chunk_len, n_q_heads,
+                                                               n_kv_heads, page_size))
+
+
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace buffer (the library keeps it zeroed where it must be)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def tq4_attn_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """q [batch][n_q][256] bf16; page_table int32 [batch][stride]; seq_lens int32 [batch]."""
+    batch, n_q, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                 pool.page_size), q.device)
+    ps = pool.struct()
+    check(load_library().tq4_attn_decode(
+        ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+        _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tq4_attn_prefill_chunk(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor,
+                           prior_len: int, scale: float, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q [chunk_len][n_q][256] bf16; page_table int32 covering prior_len + chunk_len positions."""
+    chunk_len, n_q, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_attn_prefill_workspace_size(prior_len, chunk_len, n_q, pool.n_kv,
+                                                                  pool.page_size), q.device)
+    ps = pool.struct()
+    check(load_library().tq4_attn_prefill_chunk(
+        ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(prior_len), chunk_len, n_q,
+        float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out

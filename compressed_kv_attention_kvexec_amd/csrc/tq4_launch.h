@@ -1,0 +1,101 @@
+// tq4_launch.h -- host-side launch interface between the C ABI layer and the
+// gfx950 kernels.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq4 {
+
+struct Codebook {
+    float centroid[16];   // ascending fp32 centroids (Lloyd-Max levels of N(0,1) / 16)
+    float threshold[15];  // fp32 midpoints of adjacent centroids
+};
+
+// Host-computed codec constants (computed once, thread-safe).
+const Codebook &codebook();
+
+struct EncodeParams {
+    uint32_t *words[2];  // K, V (NULL: skip that half)
+    uint16_t *norms[2];
+    const void *src[2];
+    int src_bf16;
+    const int32_t *slots;
+    int32_t n_tokens;
+    int32_t n_kv;
+    int32_t page_size;
+    int32_t num_slots;  // num_pages * page_size
+};
+
+hipError_t launch_encode(const EncodeParams &p, hipStream_t stream);
+
+// Split-K plan of one decode call; a pure function of the sizes so the
+// workspace query needs no device.
+struct DecodePlan {
+    int32_t group;        // n_q_heads / n_kv_heads
+    int32_t n_splits;     // workgroups per (request, KV head)
+    int32_t split_tiles;  // 32-key tiles per workgroup
+    size_t counters_bytes;
+    size_t partial_floats;  // floats per (request, KV head, split)
+    size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads);
+
+struct DecodeParams {
+    const uint32_t *k_words;
+    const uint32_t *v_words;
+    const uint16_t *k_norms;
+    const uint16_t *v_norms;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv;
+    const uint16_t *q;  // bf16 bits [batch][n_q][256]
+    const int32_t *page_table;
+    int32_t table_stride;
+    const int32_t *seq_lens;
+    int32_t batch;
+    int32_t max_seq_len;
+    int32_t n_q;
+    float scale;
+    uint16_t *out;  // bf16 bits [batch][n_q][256]
+    void *workspace;
+};
+
+hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStream_t stream);
+
+struct PrefillPlan {
+    int32_t group;
+    int32_t q_tokens_per_block;  // chunk tokens per query block
+    int32_t n_qblocks;
+    int32_t n_splits;            // key splits per (query block, KV head)
+    int32_t split_tiles;
+    size_t counters_bytes;
+    size_t partial_floats;
+    size_t workspace_bytes;
+};
+
+PrefillPlan plan_prefill(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads, int32_t n_kv_heads);
+
+struct PrefillParams {
+    const uint32_t *k_words;
+    const uint32_t *v_words;
+    const uint16_t *k_norms;
+    const uint16_t *v_norms;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv;
+    const uint16_t *q;  // bf16 [chunk][n_q][256]
+    const int32_t *page_table;
+    int32_t prior_len;
+    int32_t chunk_len;
+    int32_t n_q;
+    float scale;
+    uint16_t *out;
+    void *workspace;
+};
+
+hipError_t launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream);
+
+}  // namespace tq4

@@ -1,0 +1,206 @@
+/*
+ * tq4.h -- C ABI of the TQ4 paged-KV attention library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What the library computes (sources cited by page title and section):
+ *
+ *   [KVX] "Fitting a 27B-Parameter LLM into 24 GiB of Laptop Memory"
+ *         (simpleprog.com article on the JustFit preprint), section
+ *         "KVExec: Fused Reconstruction with Layer-Scoped Lifetime".
+ *         Each cached key or value vector is one TQ4 record: 32 u32 words,
+ *         eight 4-bit centroid indices per word (256 dims), plus one fp16
+ *         norm.  Attention reads packed page IDs, looks the indices up in a
+ *         16-entry centroid table, undoes the Hadamard rotation, restores the
+ *         norm and feeds scaled dot-product attention at once; the attention
+ *         result is complete before the call's work ends, and no
+ *         full-precision K/V is ever written to memory.  Single-query decode
+ *         works on the compressed pages directly; multi-query prefill
+ *         reconstructs tiles and runs a floating-point attention consumer.
+ *   [MBE] same page, section "The Memory Budget Equation": 4 KV heads of
+ *         dimension 256 per full-attention layer.
+ *   [ST]  same page, section "StateTrans: Request Transitions at Safe
+ *         Boundaries": 256-token pages, page IDs shared between requests with
+ *         a common prefix.
+ *   [P5]  "JustFit: Run Qwen 27B Fast with its full 256K context on a 24 GB
+ *         Mac" (wpnews.pro), mechanism table, KVExec row: bounded
+ *         reconstruction and attention in the rotated domain.
+ *
+ * Codec conventions the pages leave open (the library and its tests use these):
+ *   - dim 8k+j of a vector is held in bits 4j..4j+3 of word k;
+ *   - index i selects the i-th smallest of 16 fp32 centroids, which are the
+ *     16-level Lloyd-Max levels of N(0,1) divided by 16;
+ *   - the rotation is H/16 with H the natural-order Sylvester Hadamard matrix
+ *     of order 256 (symmetric and orthonormal, so it is its own inverse);
+ *   - the norm is ||x||_2 of the source vector, rounded to fp16; the rotated
+ *     unit vector H x / (16 ||x||) is what is quantised;
+ *   - encoding is fp32, round-to-nearest-even, no fused multiply-add: squares
+ *     summed by the stride-halving tree (128, 64, ..., 1), correctly rounded
+ *     sqrt, Hadamard butterflies (a, b) -> (a + b, a - b) in ascending stage
+ *     order 1, 2, ..., 128, index = number of thresholds t_i = b_i * (16 n)
+ *     strictly below the rotated coordinate, b_i the fp32 midpoints of
+ *     adjacent centroids.
+ *   - query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *
+ * Memory layout of one layer's pool (all device memory, caller-owned):
+ *   k_words, v_words : uint32 [num_pages][n_kv_heads][page_size][32]
+ *   k_norms, v_norms : fp16 bits [num_pages][n_kv_heads][page_size]
+ * A slot is page_id * page_size + offset.  Position p of a request lives in
+ * page page_table[p / page_size] at offset p % page_size.  One page ID names
+ * the same slot range in every layer's pool.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every buffer; the library never allocates,
+ *     frees or synchronises, and keeps no mutable global state.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; calls are thread-safe.  Calls that share a
+ *     workspace must be ordered on one stream.
+ *   - Errors: every argument check happens on the host before any HIP call,
+ *     so a non-OK status means nothing was enqueued (except TQ4_ERR_HIP,
+ *     which reports a failed launch).  No exception or abort crosses the ABI.
+ *   - Device data (page tables, sequence lengths, slots) is not read on the
+ *     host.  A sequence length is clamped to [0, max]; a page ID or slot
+ *     outside the pool is skipped (its positions are masked, its record is
+ *     not written), so bad device data never makes the library touch memory
+ *     outside the buffers described here.
+ */
+#ifndef TQ4_H
+#define TQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ4_ABI_VERSION 1
+#define TQ4_HEAD_DIM 256
+#define TQ4_WORDS_PER_VECTOR 32
+#define TQ4_NUM_CENTROIDS 16
+#define TQ4_MAX_GROUP 16 /* largest n_q_heads / n_kv_heads */
+
+typedef enum tq4_status {
+    TQ4_OK = 0,
+    TQ4_ERR_NULL = 1,      /* a required pointer is NULL */
+    TQ4_ERR_SHAPE = 2,     /* a size is out of range or inconsistent */
+    TQ4_ERR_DTYPE = 3,     /* unsupported element type */
+    TQ4_ERR_ALIGN = 4,     /* a pointer is not aligned as documented */
+    TQ4_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+    TQ4_ERR_HIP = 6        /* the HIP runtime reported an error */
+} tq4_status;
+
+typedef enum tq4_dtype {
+    TQ4_F32 = 0,
+    TQ4_BF16 = 1,
+    TQ4_F16 = 2
+} tq4_dtype;
+
+/* One layer's page pool.  Words need 16-byte alignment, norms 8-byte.
+ * Limits: head_dim == 256; page_size a multiple of 32 in [32, 1024];
+ * num_pages >= 1; n_kv_heads >= 1; num_pages * n_kv_heads * page_size < 2^31. */
+typedef struct tq4_layer_pool {
+    uint32_t *k_words;
+    uint32_t *v_words;
+    uint16_t *k_norms;
+    uint16_t *v_norms;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+} tq4_layer_pool;
+
+/* TQ4_ABI_VERSION of the loaded library. */
+int tq4_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char *tq4_status_string(tq4_status status);
+
+/* Host copy of the codec constants: the 16 fp32 centroids in ascending order
+ * and the 15 fp32 decision thresholds (midpoints of adjacent centroids).
+ * Both pointers are host memory.  Returns TQ4_ERR_NULL on a NULL pointer. */
+tq4_status tq4_codebook(float centroids[16], float thresholds[15]);
+
+/*
+ * tq4_encode_pages -- write TQ4 records for n_tokens new positions
+ * ([KVX]: the cache is kept as TQ4 pages; a position's K and V are encoded
+ * when they are written).
+ *
+ *   k, v      : device, [n_tokens][n_kv_heads][256] in src_dtype (TQ4_F32 or
+ *               TQ4_BF16), 16-byte aligned.  Either may be NULL (that half of
+ *               the pool is left untouched), not both.
+ *   slots     : device int32 [n_tokens]; record t is written at slot slots[t]
+ *               of every KV head.  A slot outside [0, num_pages * page_size)
+ *               is skipped.  Two tokens with one slot race.
+ *   n_tokens  : >= 0 (0 enqueues nothing).
+ * The result is bit-identical to the conventions above for every input.
+ */
+tq4_status tq4_encode_pages(const tq4_layer_pool *pool, const void *k, const void *v,
+                            tq4_dtype src_dtype, const int32_t *slots, int32_t n_tokens,
+                            void *stream);
+
+/*
+ * Bytes of device workspace tq4_attn_decode needs for these sizes (0 for
+ * invalid sizes).  It grows with batch and KV heads, not with the sequence
+ * length beyond a fixed split cap, so no per-position scratch exists.
+ */
+size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t page_size);
+
+/*
+ * tq4_attn_decode -- single-query attention for each request directly on the
+ * packed pages ([KVX]; rotated-domain formulation of [P5]).
+ *
+ *   q         : device [batch][n_q_heads][256], q_dtype == TQ4_BF16, 16-byte
+ *               aligned.
+ *   page_table: device int32 [batch][page_table_stride].
+ *   seq_lens  : device int32 [batch]; cached positions of each request,
+ *               including the current token (already encoded).  Clamped to
+ *               [0, max_seq_len]; a request with 0 positions gets a zero output.
+ *   max_seq_len: host upper bound of seq_lens, 1 <= max_seq_len <=
+ *               page_table_stride * page_size; it sets the launch plan.
+ *   n_q_heads : a multiple of n_kv_heads with n_q_heads / n_kv_heads <= 16.
+ *   scale     : softmax scale applied to q.k (1/16 = 1/sqrt(256) usually).
+ *   out       : device [batch][n_q_heads][256] in q_dtype, 16-byte aligned;
+ *               out[b][h] = sum_j softmax_j(scale q.k_j) v_j.
+ *   workspace : device, >= tq4_attn_decode_workspace_size(...) bytes,
+ *               256-byte aligned, ZERO-FILLED before its first use; every call
+ *               leaves it zero-filled again where it must be, so it can be
+ *               reused call after call on one stream.
+ */
+tq4_status tq4_attn_decode(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
+                           const int32_t *page_table, int32_t page_table_stride,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                           int32_t n_q_heads, float scale, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace tq4_attn_prefill_chunk needs (0 for invalid sizes). */
+size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,
+                                       int32_t n_kv_heads, int32_t page_size);
+
+/*
+ * tq4_attn_prefill_chunk -- causal attention of a chunk of chunk_len query
+ * tokens over prior_len cached positions plus the chunk itself ([KVX]:
+ * multi-query prefill reconstructs K/V tiles and runs a floating-point
+ * attention consumer; here the tiles are reconstructed in the rotated domain
+ * in on-chip memory and consumed by matrix-core products).
+ *
+ *   q         : device [chunk_len][n_q_heads][256] in q_dtype == TQ4_BF16,
+ *               16-byte aligned; token t sits at absolute position
+ *               prior_len + t and attends positions 0 .. prior_len + t.
+ *   page_table: device int32 covering prior_len + chunk_len positions.  The
+ *               chunk's own K/V must already be encoded into the pool.
+ *   prior_len : >= 0; chunk_len >= 1.
+ *   out       : device [chunk_len][n_q_heads][256] in q_dtype.
+ *   workspace : device, >= tq4_attn_prefill_workspace_size(...) bytes,
+ *               256-byte aligned, zero-filled before first use (as for decode).
+ */
+tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
+                                  const int32_t *page_table, int32_t prior_len, int32_t chunk_len,
+                                  int32_t n_q_heads, float scale, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ4_H */
