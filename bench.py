@@ -1,0 +1,216 @@
+"""Benchmark: TQ4 decode attention over a paged 4-bit KV cache on one MI355X.
+
+A step is one decode step of all 16 full-attention layers at 212,992 cached
+positions (196,608 prompt + 16,384 generated; 4 KV heads x 256 dims, 24 bf16
+query heads, 256-token pages shuffled in a 229,376-position pool, one pool per
+layer): per layer, the current token's K and V are encoded into its slot
+(tq4_encode_pages) and the query attends all cached positions
+(tq4_attn_decode).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TQ4 decode-attn cached positions/s & HBM GB/s (% peak) at 212,992 ctx"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix
+TQ4_BYTES_PER_POS_LAYER = 4 * 2 * 130  # 4 KV heads x (K, V) x (128 B words + 2 B norm)
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_algorithmic_bytes(seq_lens, page_size: int, n_q: int) -> int:
+    """Bytes one decode launch must move: TQ4 records of every attended position,
+    the queries, the output and the page-table entries (and lengths) it reads."""
+    pages = sum(-(-L // page_size) for L in seq_lens)
+    return (sum(seq_lens) * TQ4_BYTES_PER_POS_LAYER + len(seq_lens) * n_q * 256 * 2 * 2
+            + pages * 4 + len(seq_lens) * 4)
+
+
+def build_layers(w, device):
+    """Per layer: pool, page table, lengths, query, current-token K/V and slot (GPU-encoded)."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    import synth
+    layers = []
+    chunk = 32768
+    for layer in range(w.n_layers):
+        table = synth.placement(w, layer)
+        slots = synth.used_slots(w, table)
+        pool = tq4.Tq4LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+        slots_d = torch.from_numpy(slots).to(device)
+        for which, seed_t in ((0, synth.T_K), (1, synth.T_V)):
+            src = synth.torch_normal(synth.seed_of(w.wid, layer, seed_t), (len(slots), w.n_kv, 256), device)
+            for c0 in range(0, len(slots), chunk):
+                part = src[c0:c0 + chunk]
+                if which == 0:
+                    tq4.tq4_encode_pages(pool, part, None, slots_d[c0:c0 + chunk])
+                else:
+                    tq4.tq4_encode_pages(pool, None, part, slots_d[c0:c0 + chunk])
+            del src
+        # the current token (last position of every request) is re-encoded inside each step
+        last = []
+        for b, L in enumerate(w.seq_lens):
+            p = L - 1
+            last.append(int(table[b, p // w.page_size]) * w.page_size + p % w.page_size)
+        gen = torch.Generator(device=device)
+        gen.manual_seed(synth.seed_of(w.wid, layer, 7))
+        k_new = torch.randn((len(last), w.n_kv, 256), generator=gen, device=device)
+        v_new = torch.randn((len(last), w.n_kv, 256), generator=gen, device=device)
+        q = synth.torch_normal(synth.seed_of(w.wid, layer, synth.T_Q), (w.batch, w.n_q, 256), device)
+        layers.append(dict(pool=pool, table=torch.from_numpy(table).to(device),
+                           seq=torch.tensor(w.seq_lens, dtype=torch.int32, device=device),
+                           q=q.to(torch.bfloat16).contiguous(), k_new=k_new, v_new=v_new,
+                           slot_new=torch.tensor(last, dtype=torch.int32, device=device)))
+        torch.cuda.synchronize()
+        log(f"layer {layer}: pool built ({len(slots)} positions encoded)")
+    return layers
+
+
+def cpu_baseline(sample_positions: int):
+    """The oracle (plain single-threaded C, fp64) on a bounded sample of the same
+    workload: one layer, the first `sample_positions` cached positions, one
+    request, all 24 query heads.  Pool building by the oracle is not timed."""
+    import numpy as np
+    import oracle
+    import synth
+    w0 = synth.WORKLOADS["decode_212k_16l"]
+    w = synth.Workload(w0.wid, "sample", "decode", 1, w0.page_size, w0.pool_pages,
+                       seq_lens=(sample_positions,))
+    table = synth.placement(w, 0)
+    slots = synth.used_slots(w, table)
+    pool = oracle.Pool.empty(w.pool_pages, w.n_kv, w.page_size)
+    oracle.encode_to_pool(pool, synth.kv_source(w, 0, len(slots), synth.T_K),
+                          synth.kv_source(w, 0, len(slots), synth.T_V), slots)
+    q = synth.bf16_round(synth.queries_f32(w, 0, 1)).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.attn_decode(pool, q, table, [sample_positions], synth.SCALE)
+    dt = time.perf_counter() - t0
+    per_pos_16l = dt / sample_positions * 16  # seconds per cached position over 16 layers
+    return {"value": 1.0 / per_pos_16l, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": (f"1 layer x {sample_positions} cached positions x 24 query heads, one decode query; "
+                       f"{dt:.2f} s, scaled to 16 layers"),
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_212k_16l")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-positions", type=int, default=131072)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    assert w.kind == "decode"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tq4.load_library()
+    log(f"workload {w.name}: {w.n_layers} layers, seq_lens {w.seq_lens}")
+    layers = build_layers(w, dev)
+
+    ws_bytes = tq4.tq4_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv, w.page_size)
+    workspace = tq4.new_workspace(ws_bytes, dev)
+    outs = [torch.empty_like(L["q"]) for L in layers]
+    stream = torch.cuda.current_stream()
+    enc_calls = [tq4.prepare_encode(L["pool"], L["k_new"], L["v_new"], L["slot_new"], stream) for L in layers]
+    dec_calls = [tq4.prepare_decode(L["pool"], L["q"], L["table"], L["seq"], max(w.seq_lens), synth.SCALE,
+                                    outs[i], workspace, stream) for i, L in enumerate(layers)]
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
+
+    def step(events=None):
+        for i in range(w.n_layers):
+            enc_calls[i]()
+            if events is not None:
+                events[i][0].record(stream)
+            dec_calls[i]()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.n_layers)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
+    avg_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
+    log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.3f} ms/step, "
+        f"decode kernel avg {avg_dec_s * 1e6:.1f} us")
+
+    # outputs must be finite (a cheap guard that the timed work produced results)
+    for o in outs:
+        if not torch.isfinite(o.float()).all():
+            raise RuntimeError("non-finite decode output")
+
+    positions = sum(w.seq_lens)  # cached positions per step, each across all layers
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = positions / (elapsed / args.steps)
+    bytes_launch = decode_algorithmic_bytes(w.seq_lens, w.page_size, w.n_q)
+    achieved = bytes_launch / avg_dec_s / 1e9
+    step_gbs = bytes_launch * w.n_layers / (elapsed / args.steps) / 1e9
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "batch": w.batch,
+                   "cached_positions": list(w.seq_lens), "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
+                   "head_dim": 256, "page_size": w.page_size, "pool_pages": w.pool_pages,
+                   "query_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tq4_decode_kernel", "bytes_per_launch": bytes_launch,
+                     "avg_launch_us": avg_dec_s * 1e6},
+        "extra": {"step_hbm_gb_per_s": step_gbs, "step_frac_of_peak": step_gbs / HBM_PEAK_GBS,
+                  "decode_launches_timed": len(dec_ms)},
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample_positions} positions ...")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_sample_positions)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

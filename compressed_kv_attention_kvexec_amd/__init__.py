@@ -20,7 +20,8 @@ from ._binding import (TQ4_BF16, TQ4_F16, TQ4_F32, Tq4Error, check, header_funct
 
 __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_encode_pages",
            "tq4_attn_decode_workspace_size", "tq4_attn_decode", "tq4_attn_prefill_workspace_size",
-           "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library"]
+           "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library",
+           "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill"]
 
 HEAD_DIM = 256
 WORDS = 32
@@ -154,3 +155,48 @@ def tq4_attn_prefill_chunk(pool: Tq4LayerPool, q: torch.Tensor, page_table: torc
         float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out
+
+
+class PreparedCall:
+    """A library call with its ctypes arguments marshalled once.
+
+    Calling it repeats the same C call (same pointers, same stream), which
+    keeps Python overhead out of tight launch loops such as a decode step over
+    many layers.  The tensors it was built from must stay alive."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            check(st)
+
+
+def prepare_encode(pool: Tq4LayerPool, k, v, slots: torch.Tensor, stream=None) -> PreparedCall:
+    src = k if k is not None else v
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(k), _ptr(v), _dtype_code(src), _ptr(slots), int(slots.shape[0]),
+            _stream(stream))
+    return PreparedCall(load_library().tq4_encode_pages, args, (ps, pool, k, v, slots))
+
+
+def prepare_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                   max_seq_len: int, scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                   stream=None) -> PreparedCall:
+    batch, n_q, _ = q.shape
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+            _ptr(seq_lens), batch, int(max_seq_len), n_q, ctypes.c_float(scale), _ptr(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return PreparedCall(load_library().tq4_attn_decode, args, (ps, pool, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_prefill(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, prior_len: int,
+                    scale: float, out: torch.Tensor, workspace: torch.Tensor, stream=None) -> PreparedCall:
+    chunk_len, n_q, _ = q.shape
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(prior_len), chunk_len, n_q,
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return PreparedCall(load_library().tq4_attn_prefill_chunk, args, (ps, pool, q, page_table, out, workspace))

@@ -122,8 +122,9 @@ tq4_status tq4_attn_decode(const tq4_layer_pool *pool, const void *q, tq4_dtype 
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return TQ4_ERR_ALIGN;
     const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads);
-    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return TQ4_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return TQ4_ERR_ALIGN;
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return TQ4_ERR_WORKSPACE;
+    if (workspace != nullptr && !aligned(workspace, 256)) return TQ4_ERR_ALIGN;
     tq4::DecodeParams p{};
     p.k_words = pool->k_words;
     p.v_words = pool->v_words;

@@ -140,8 +140,9 @@ tq4_status tq4_encode_pages(const tq4_layer_pool *pool, const void *k, const voi
 
 /*
  * Bytes of device workspace tq4_attn_decode needs for these sizes (0 for
- * invalid sizes).  It grows with batch and KV heads, not with the sequence
- * length beyond a fixed split cap, so no per-position scratch exists.
+ * invalid sizes, and 0 when one workgroup covers each request and KV head).
+ * It grows with batch and KV heads, not with the sequence length beyond a
+ * fixed split cap, so no per-position scratch exists.
  */
 size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t page_size);
@@ -163,9 +164,10 @@ size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_
  *   out       : device [batch][n_q_heads][256] in q_dtype, 16-byte aligned;
  *               out[b][h] = sum_j softmax_j(scale q.k_j) v_j.
  *   workspace : device, >= tq4_attn_decode_workspace_size(...) bytes,
- *               256-byte aligned, ZERO-FILLED before its first use; every call
- *               leaves it zero-filled again where it must be, so it can be
- *               reused call after call on one stream.
+ *               256-byte aligned (may be NULL when that size is 0).  It holds
+ *               per-split partial results between the call's two kernels; its
+ *               contents on entry do not matter.  Calls sharing a workspace
+ *               must be ordered on one stream.
  */
 tq4_status tq4_attn_decode(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
                            const int32_t *page_table, int32_t page_table_stride,

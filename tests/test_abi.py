@@ -40,8 +40,8 @@ def test_codebook_matches_oracle_bitwise(lib, oracle_mod):
     assert lib.tq4_codebook(None, b) == 1
 
 
-def _decode(lib, pool=None, q=FAKE, q_dtype=B.TQ4_BF16, table=FAKE, stride=4, seq=FAKE, batch=1,
-            max_seq=200, n_q=24, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+def _decode(lib, pool=None, q=FAKE, q_dtype=B.TQ4_BF16, table=FAKE, stride=64, seq=FAKE, batch=1,
+            max_seq=4000, n_q=24, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
     pool = _pool() if pool is None else pool
     return lib.tq4_attn_decode(ctypes.byref(pool), q, q_dtype, table, stride, seq, batch, max_seq,
                                n_q, 0.0625, out, ws, ws_bytes, None)
@@ -63,13 +63,14 @@ def test_decode_validation(lib):
     assert _decode(lib, n_q=68) == 2           # group of 17 > 16
     assert _decode(lib, batch=0) == 2
     assert _decode(lib, max_seq=0) == 2
-    assert _decode(lib, max_seq=257) == 2      # beyond stride * page_size = 256
+    assert _decode(lib, max_seq=4097) == 2     # beyond stride * page_size = 4096
     assert _decode(lib, q=FAKE + 2) == 4
     assert _decode(lib, out=FAKE + 8) == 4
     assert _decode(lib, pool=_pool(ptr=FAKE + 4)) == 4
     assert _decode(lib, ws=None) == 5
-    need = lib.tq4_attn_decode_workspace_size(1, 200, 24, 4, 64)
+    need = lib.tq4_attn_decode_workspace_size(1, 4000, 24, 4, 64)
     assert need > 0
+    assert lib.tq4_attn_decode_workspace_size(1, 200, 24, 4, 64) == 0  # one split, no scratch
     assert _decode(lib, ws_bytes=need - 1) == 5
     assert _decode(lib, ws=FAKE + 128) == 4
 
