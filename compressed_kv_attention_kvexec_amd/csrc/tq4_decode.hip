@@ -31,14 +31,12 @@
 
 #include "tq4_device.h"
 #include "tq4_launch.h"
+#include "tq4_tile.h"
 
 namespace tq4 {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr int kTile = 32;
-constexpr int kLutEntries = 256;
-constexpr int kLutWords = kLutEntries * kWave;  // 64 KiB
 constexpr int kMaxSplits = 256;
 constexpr int kPlanCUs = 256;       // MI355X compute units
 constexpr int kPlanWgsPerCU = 1;    // resident decode workgroups per CU
@@ -74,130 +72,6 @@ DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, in
     pl.workspace_bytes = pl.n_splits > 1 ? static_cast<size_t>(units) * pl.n_splits * pl.partial_floats * sizeof(float)
                                          : 0;
     return pl;
-}
-
-// ---------------------------------------------------------------- device helpers
-
-// Registers of one 32-key tile held by a lane (lane = 16 * gq + n).
-struct KRegs {
-    u32x4 k[2][2];   // [M-tile][half]: words 16*half + 4*gq .. +3 of key 16*mt + n
-    u32x2 kn[2];     // K norms of keys 4gq..4gq+3 and 16+4gq..16+4gq+3
-};
-struct VRegs {
-    u32x2 v[8];      // words 2n, 2n+1 of key sigma(j) = j < 4 ? 4gq + j : 16 + 4gq + j - 4
-    u32x2 vn[2];     // V norms of the same keys as kn
-};
-// 8 nibbles of one word -> 8 fp16 values (dim order) via the lane-private LDS table.
-__device__ __forceinline__ half8 lut_decode(uint32_t w, uint32_t lane4, const char *lut) {
-    const uint32_t a0 = perm(w, lane4, 0x0c0c0400u);
-    const uint32_t a1 = perm(w, lane4, 0x0c0c0500u);
-    const uint32_t a2 = perm(w, lane4, 0x0c0c0600u);
-    const uint32_t a3 = perm(w, lane4, 0x0c0c0700u);
-    u32x4 r;
-    r.x = *reinterpret_cast<const uint32_t *>(lut + a0);
-    r.y = *reinterpret_cast<const uint32_t *>(lut + a1);
-    r.z = *reinterpret_cast<const uint32_t *>(lut + a2);
-    r.w = *reinterpret_cast<const uint32_t *>(lut + a3);
-    return __builtin_bit_cast(half8, r);
-}
-
-// Transpose an 8x8 block of nibbles: in[j] nibble i -> out[i] nibble j.
-__device__ __forceinline__ void nibble_transpose8(const uint32_t in[8], uint32_t out[8]) {
-    uint32_t a[8], b[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        a[j] = perm(in[j + 4], in[j], 0x05040100u);      // low halves
-        a[j + 4] = perm(in[j + 4], in[j], 0x07060302u);  // high halves
-    }
-#pragma unroll
-    for (int k = 0; k < 8; k += 4) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int x = k + kk;
-            b[x] = perm(a[x + 2], a[x], 0x06020400u);
-            b[x + 2] = perm(a[x + 2], a[x], 0x07030501u);
-        }
-    }
-    const uint32_t m = 0x0f0f0f0fu;
-#pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-        out[k] = (b[k] & m) | ((b[k + 1] << 4) & ~m);
-        out[k + 1] = ((b[k] >> 4) & m) | (b[k + 1] & ~m);
-    }
-}
-
-__device__ __forceinline__ float f16lo(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w)); }
-__device__ __forceinline__ float f16hi(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w >> 16)); }
-
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_f16_bits(lo)) | (static_cast<uint32_t>(f32_to_f16_bits(hi)) << 16);
-}
-
-// First record of a tile (page `pid`, in-page offset of key0); page IDs outside the pool map to
-// page 0 and the tile is masked.
-__device__ __forceinline__ int64_t tile_rec0(const DecodeParams &p, int g, int key0, int pid, bool &valid) {
-    const int page_idx = key0 / p.page_size;
-    const int off0 = key0 - page_idx * p.page_size;
-    valid = (pid >= 0 && pid < p.num_pages);
-    if (!valid) pid = 0;
-    return (static_cast<int64_t>(pid) * p.n_kv + g) * p.page_size + off0;
-}
-
-// Tile loads address a wave-uniform record base (scalar registers) plus fixed per-lane byte
-// offsets, so each load is one instruction with no per-tile vector address arithmetic.
-struct LaneOffsets {
-    uint32_t k;   // (n * 32 + 4 * gq) words -> bytes; + 2048 per M-tile, + 64 per half
-    uint32_t v;   // key 4gq, words 2n -> bytes; keys 4gq+j at + 128 j, keys 16+4gq+j at + 2048 + 128 j
-    uint32_t nrm; // norms of key 4gq -> bytes; + 32 for keys 16+4gq..
-};
-
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
-    const uint32_t n = lane & 15, gq = lane >> 4;
-    return {n * 128u + gq * 16u, gq * 512u + n * 8u, gq * 8u};
-}
-
-__device__ __forceinline__ void load_k(const DecodeParams &p, int64_t rec0, const LaneOffsets &o, KRegs &t) {
-    const char *wb = reinterpret_cast<const char *>(p.k_words) + rec0 * (kWords * 4);
-    const char *nb = reinterpret_cast<const char *>(p.k_norms) + rec0 * 2;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) t.k[mt][h] = *reinterpret_cast<const u32x4 *>(wb + o.k + (2048u * mt + 64u * h));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) t.kn[h] = *reinterpret_cast<const u32x2 *>(nb + o.nrm + 32u * h);
-}
-
-__device__ __forceinline__ void load_v(const DecodeParams &p, int64_t rec0, const LaneOffsets &o, VRegs &t) {
-    const char *wb = reinterpret_cast<const char *>(p.v_words) + rec0 * (kWords * 4);
-    const char *nb = reinterpret_cast<const char *>(p.v_norms) + rec0 * 2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t koff = (j < 4) ? 128u * j : 2048u + 128u * (j - 4);
-        t.v[j] = *reinterpret_cast<const u32x2 *>(wb + o.v + koff);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) t.vn[h] = *reinterpret_cast<const u32x2 *>(nb + o.nrm + 32u * h);
-}
-
-// Unnormalised Hadamard transform of one 256-vector held by a wavefront, lane l holding dims
-// 4l .. 4l+3: stages 1 and 2 in registers, stages 4 .. 128 pair lane l with lane l ^ (h / 4).
-__device__ __forceinline__ void wave_fwht(float y[4], int lane) {
-    {
-        const float t0 = y[0] + y[1], t1 = y[0] - y[1], t2 = y[2] + y[3], t3 = y[2] - y[3];
-        y[0] = t0 + t2;
-        y[2] = t0 - t2;
-        y[1] = t1 + t3;
-        y[3] = t1 - t3;
-    }
-#pragma unroll
-    for (int m = 1; m <= 32; m <<= 1) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float o = __shfl_xor(y[r], m, kWave);
-            y[r] = upper ? (o - y[r]) : (y[r] + o);
-        }
-    }
 }
 
 // ---------------------------------------------------------------- split kernel
@@ -263,15 +137,7 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
 
     // ---- prologue: zero the query operand, fill the centroid table, rotate the group's queries
     reinterpret_cast<u32x4 *>(&qop_sh[0][0])[tid] = u32x4{0u, 0u, 0u, 0u};  // 512 x 16 B
-    // centroid table: entry e (a nibble pair) -> fp16x2 (16 c[e & 15], 16 c[e >> 4]); one copy per
-    // lane, so a 256-byte row per entry, written 16 bytes at a time
-    for (int i = tid; i < kLutWords / 4; i += kDecThreads) {
-        const int e = i >> 4;
-        const uint32_t lo = (a.lut_pairs[(e & 15) >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t hi = (a.lut_pairs[(e >> 4) >> 1] >> (16 * ((e >> 4) & 1))) & 0xffffu;
-        const uint32_t v = lo | (hi << 16);
-        reinterpret_cast<u32x4 *>(lut_mem)[i] = u32x4{v, v, v, v};
-    }
+    build_lut(lut_mem, a.lut_pairs, tid, kDecThreads);
     __syncthreads();
     for (int h = wave; h < G; h += kDecWaves) {
         // one wavefront rotates query head h: y = H q (unnormalised), then a power-of-two scale
@@ -283,12 +149,7 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
         wave_fwht(y, lane);
         float mx = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
         for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
-        int e = 0;
-        if (mx > 0.f) {
-            int E;
-            frexpf(mx, &E);
-            e = 14 - E;
-        }
+        const int e = q_exponent(mx);
         const float qs = ldexpf(1.0f, e);
         if (lane == 0) head_f[h] = p.scale * 1.4426950408889634f * ldexpf(1.0f, -e) * (1.0f / 256.0f);
         // dims 4l .. 4l+3 sit in word w = l / 2 at slots 4 (l & 1) ..; word w feeds K-step
@@ -354,11 +215,13 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
         const float m_new = fmaxf(m_run, mx);
         // this lane's accumulators all belong to head n, so the rescale factor is lane-local
-        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        m_run = m_new;
-        l_run *= alpha;
+        if (__any(m_new > m_run)) {  // rare once the running maxima settle
+            const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) oacc[tt] *= alpha;
+            for (int tt = 0; tt < 16; ++tt) oacc[tt] *= alpha;
+            m_run = m_new;
+        }
         float pv[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -499,63 +362,79 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
 // One workgroup per (query head, KV head, request): merges the split partials of that head in
 // fixed split order (max-rescaled sums), applies the inverse rotation and writes bf16.
 
-constexpr int kCombThreads = 256;
+constexpr int kCombQuarters = 4;
+constexpr int kCombThreads = kDim * kCombQuarters;
 
 __global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(DecodeArgs a) {
     __shared__ float wgt[kMaxSplits];
     __shared__ float sL[kMaxSplits];
-    __shared__ float row[kDim];
-    __shared__ float totL;
+    __shared__ float part[kCombQuarters][kDim];
     const DecodeParams &p = a.p;
     const int G = a.group;
     const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int d = threadIdx.x;
+    const int tid = threadIdx.x, d = tid & (kDim - 1), qtr = tid / kDim;
+    const size_t pf = static_cast<size_t>(a.partial_floats);
+    const float *base = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + a.parts_off) +
+                        (static_cast<size_t>(b) * p.n_kv + g) * a.n_splits * pf;
+    // Every load is issued before the sequence length is known: slots past the live splits hold
+    // stale data, so they are dropped by selection below, never multiplied in.
+    const int ns = a.n_splits;
+    float m_k = -INFINITY, l_k = 0.f;
+    if (tid < ns) {
+        m_k = base[tid * pf + h];
+        l_k = base[tid * pf + 16 + h];
+    }
+    const float *col = base + 32 + h * kDim + d;
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int k = qtr + kCombQuarters * u;
+        v[u] = k < ns ? col[k * pf] : 0.f;
+    }
     int L = p.seq_lens[b];
     L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
     const int split_keys = a.split_tiles * kTile;
     const int n_active = (L + split_keys - 1) / split_keys;
     if (n_active <= 1) return;  // the split kernel wrote this output itself
-    const size_t pf = static_cast<size_t>(a.partial_floats);
-    const float *base = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + a.parts_off) +
-                        (static_cast<size_t>(b) * p.n_kv + g) * a.n_splits * pf;
-    for (int k = d; k < n_active; k += kCombThreads) {
-        wgt[k] = base[k * pf + h];
-        sL[k] = base[k * pf + 16 + h];
+    if (tid < n_active) {
+        wgt[tid] = m_k;
+        sL[tid] = l_k;
     }
     __syncthreads();
     float M = -INFINITY;
     for (int k = 0; k < n_active; ++k) M = fmaxf(M, wgt[k]);
     __syncthreads();
-    for (int k = d; k < n_active; k += kCombThreads)
-        wgt[k] = (wgt[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(wgt[k] - M);
+    if (tid < n_active) wgt[tid] = (m_k == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_k - M);
     __syncthreads();
-    if (d == 0) {
-        float t = 0.f;
-        for (int k = 0; k < n_active; ++k) t += wgt[k] * sL[k];
-        totL = t;
-    }
-    const float *col = base + 32 + h * kDim + d;
     float acc = 0.f;
-    int k = 0;
-    for (; k + 8 <= n_active; k += 8) {
-        float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = col[(k + u) * pf];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += wgt[k + u] * v[u];
+    for (int u = 0; u < 16; ++u) {
+        const int k = qtr + kCombQuarters * u;
+        acc += (k < n_active) ? wgt[k] * v[u] : 0.f;
     }
-    for (; k < n_active; ++k) acc += wgt[k] * col[k * pf];
-    row[d] = acc;
+    for (int k = qtr + kCombQuarters * 16; k < n_active; k += kCombQuarters) acc += wgt[k] * col[k * pf];
+    part[qtr][d] = acc;
     __syncthreads();
-    for (int hs = 1; hs < kDim; hs <<= 1) {
-        float v = row[d];
-        const float o = row[d ^ hs];
-        __syncthreads();
-        row[d] = (d & hs) ? (o - v) : (v + o);
-        __syncthreads();
+    if (tid < kWave) {
+        // wavefront 0: sum the quarters, total weight, inverse rotation in registers, output
+        const int lane = tid;
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int dd = 4 * lane + r;
+            y[r] = ((part[0][dd] + part[1][dd]) + part[2][dd]) + part[3][dd];
+        }
+        float t = 0.f;
+        for (int k = lane; k < n_active; k += kWave) t += wgt[k] * sL[k];
+        for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, kWave);
+        wave_fwht(y, lane);
+        const float f = t > 0.f ? (1.0f / 256.0f) / t : 0.f;
+        u32x2 o;
+        o.x = static_cast<uint32_t>(f32_to_bf16(y[0] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[1] * f)) << 16);
+        o.y = static_cast<uint32_t>(f32_to_bf16(y[2] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[3] * f)) << 16);
+        *reinterpret_cast<u32x2 *>(p.out + (static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G + h) * kDim +
+                                   4 * lane) = o;
     }
-    const float f = totL > 0.f ? (1.0f / 256.0f) / totL : 0.f;
-    p.out[(static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G + h) * kDim + d] = f32_to_bf16(row[d] * f);
 }
 
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStream_t stream) {
@@ -566,13 +445,7 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStrea
     a.split_tiles = plan.split_tiles;
     a.partial_floats = static_cast<int32_t>(plan.partial_floats);
     a.parts_off = plan.counters_bytes;
-    const Codebook &cb = codebook();
-    for (int k = 0; k < 8; ++k) {
-        const _Float16 lo = static_cast<_Float16>(16.0f * cb.centroid[2 * k]);
-        const _Float16 hi = static_cast<_Float16>(16.0f * cb.centroid[2 * k + 1]);
-        a.lut_pairs[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-    }
+    lut_pairs_from_codebook(a.lut_pairs, codebook().centroid);
     hipLaunchKernelGGL(tq4_decode_kernel, dim3(plan.n_splits, p.n_kv, p.batch), dim3(kDecThreads), 0, stream, a);
     if (plan.n_splits > 1)
         hipLaunchKernelGGL(tq4_decode_combine_kernel, dim3(plan.group, p.n_kv, p.batch), dim3(kCombThreads), 0,
