@@ -26,6 +26,30 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix
 TQ4_BYTES_PER_POS_LAYER = 4 * 2 * 130  # 4 KV heads x (K, V) x (128 B words + 2 B norm)
 
 
+DECODE_PROFILE = os.path.join(ROOT, "profiles", "tq4_decode_kernel_decode_212k_16l.md")
+DECODE_SOURCES = ["compressed_kv_attention_kvexec_amd/csrc/tq4_decode.hip",
+                  "compressed_kv_attention_kvexec_amd/csrc/tq4_tile.h",
+                  "compressed_kv_attention_kvexec_amd/csrc/tq4_device.h"]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed PMC summary (FETCH_SIZE + WRITE_SIZE, each
+    scaled by a 1 GiB copy), or None when the decode sources changed since it was taken."""
+    import hashlib
+    try:
+        text = open(DECODE_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if line.startswith(("traffic_bytes", "source_sha")))
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256", "").strip() != h.hexdigest()[:16]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -38,8 +62,9 @@ def decode_algorithmic_bytes(seq_lens, page_size: int, n_q: int) -> int:
             + pages * 4 + len(seq_lens) * 4)
 
 
-def build_layers(w, device):
-    """Per layer: pool, page table, lengths, query, current-token K/V and slot (GPU-encoded)."""
+def build_layers(w, device, stats=None):
+    """Per layer: pool, page table, lengths, query, current-token K/V and slot (GPU-encoded).
+    stats (dict) receives the encode throughput measured on layer 0's pool build."""
     import torch
     import compressed_kv_attention_kvexec_amd as tq4
     import synth
@@ -52,12 +77,23 @@ def build_layers(w, device):
         slots_d = torch.from_numpy(slots).to(device)
         for which, seed_t in ((0, synth.T_K), (1, synth.T_V)):
             src = synth.torch_normal(synth.seed_of(w.wid, layer, seed_t), (len(slots), w.n_kv, 256), device)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             for c0 in range(0, len(slots), chunk):
                 part = src[c0:c0 + chunk]
                 if which == 0:
                     tq4.tq4_encode_pages(pool, part, None, slots_d[c0:c0 + chunk])
                 else:
                     tq4.tq4_encode_pages(pool, None, part, slots_d[c0:c0 + chunk])
+            e1.record()
+            if stats is not None and layer == 0:
+                torch.cuda.synchronize()
+                vecs = len(slots) * w.n_kv
+                sec = e0.elapsed_time(e1) / 1e3
+                stats.setdefault("encode_vectors", 0)
+                stats.setdefault("encode_seconds", 0.0)
+                stats["encode_vectors"] += vecs
+                stats["encode_seconds"] += sec
             del src
         # the current token (last position of every request) is re-encoded inside each step
         last = []
@@ -76,6 +112,70 @@ def build_layers(w, device):
         torch.cuda.synchronize()
         log(f"layer {layer}: pool built ({len(slots)} positions encoded)")
     return layers
+
+
+def prefill_leg(device, reps: int = 3):
+    """The chunked-prefill workload: 2,048 bf16 query tokens x 24 heads over 194,560 cached
+    positions plus the chunk itself (causal inside the chunk), one layer.  Reports the call
+    time and useful matrix-core throughput (4 * heads * 256 * attended pairs)."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    import synth
+    w = synth.WORKLOADS["prefill_2k_over_194k"]
+    table = synth.placement(w, 0)
+    slots = synth.used_slots(w, table)
+    pool = tq4.Tq4LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+    sd = torch.from_numpy(slots).to(device)
+    for which, st in ((0, synth.T_K), (1, synth.T_V)):
+        src = synth.torch_normal(synth.seed_of(w.wid, 0, st), (len(slots), w.n_kv, 256), device)
+        for c in range(0, len(slots), 65536):
+            kv = (src[c:c + 65536], None) if which == 0 else (None, src[c:c + 65536])
+            tq4.tq4_encode_pages(pool, *kv, sd[c:c + 65536])
+        del src
+    q = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (w.chunk_len, w.n_q, 256), device)
+    q = q.to(torch.bfloat16).contiguous()
+    tb = torch.from_numpy(table[0]).to(device)
+    ws = tq4.new_workspace(tq4.tq4_attn_prefill_workspace_size(w.prior_len, w.chunk_len, w.n_q, w.n_kv,
+                                                               w.page_size), device)
+    out = torch.empty_like(q)
+    call = tq4.prepare_prefill(pool, q, tb, w.prior_len, synth.SCALE, out, ws)
+    call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    pairs = sum(w.prior_len + t + 1 for t in range(w.chunk_len))
+    flop = 4 * w.n_q * 256 * pairs
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite prefill output")
+    tflops = flop / (ms / 1e3) / 1e12
+    return {"workload": w.name, "ms_per_call": ms, "tflop_per_call": flop / 1e12, "achieved_tflops": tflops,
+            "peak_tflops": MFMA_F16_PEAK_TFLOPS, "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+            "query_tokens_per_s": w.chunk_len / (ms / 1e3), "calls_timed": reps}
+
+
+def hbm_read_ceiling(device, gib: int = 4, reps: int = 5) -> float:
+    """Achievable HBM read bandwidth on this GPU: a plain fp32 sum over `gib` GiB (far beyond the
+    256 MB Infinity Cache), GB/s, best of `reps`."""
+    import torch
+    x = torch.ones(gib * (1 << 30) // 4, dtype=torch.float32, device=device)
+    x.sum()
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, x.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return best
 
 
 def cpu_baseline(sample_positions: int):
@@ -112,6 +212,7 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_212k_16l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-positions", type=int, default=131072)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -131,7 +232,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     tq4.load_library()
     log(f"workload {w.name}: {w.n_layers} layers, seq_lens {w.seq_lens}")
-    layers = build_layers(w, dev)
+    build_stats = {}
+    layers = build_layers(w, dev, build_stats)
 
     ws_bytes = tq4.tq4_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv, w.page_size)
     workspace = tq4.new_workspace(ws_bytes, dev)
@@ -199,12 +301,29 @@ def main() -> int:
                    "head_dim": 256, "page_size": w.page_size, "pool_pages": w.pool_pages,
                    "query_dtype": "bf16"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "tq4_decode_kernel", "bytes_per_launch": bytes_launch,
-                     "avg_launch_us": avg_dec_s * 1e6},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "tq4_attn_decode call = tq4_decode_kernel + tq4_decode_combine_kernel",
+                     "bytes_per_launch": bytes_launch, "avg_launch_us": avg_dec_s * 1e6},
         "extra": {"step_hbm_gb_per_s": step_gbs, "step_frac_of_peak": step_gbs / HBM_PEAK_GBS,
                   "decode_launches_timed": len(dec_ms)},
     }
+    if build_stats.get("encode_seconds"):
+        vps = build_stats["encode_vectors"] / build_stats["encode_seconds"]
+        # fp32 source in (1,024 B) and one 130 B record out per vector
+        result["extra"]["encode"] = {"vectors_per_s": vps, "gb_per_s": vps * (1024 + 130) / 1e9,
+                                     "frac_of_hbm_peak": vps * (1024 + 130) / 1e9 / HBM_PEAK_GBS,
+                                     "sample": "pool build of layer 0 (K and V), 32,768-token launches"}
+    del layers, enc_calls, dec_calls, outs, workspace
+    torch.cuda.empty_cache()
+    ceiling = hbm_read_ceiling(dev)
+    result["extra"]["hbm_read_ceiling_gb_per_s"] = ceiling
+    result["extra"]["decode_frac_of_read_ceiling"] = achieved / ceiling
+    log(f"HBM read ceiling (4 GiB fp32 sum): {ceiling:.0f} GB/s")
+    if not args.no_prefill:
+        log("prefill leg ...")
+        result["extra"]["prefill"] = prefill_leg(dev)
+        log(f"prefill: {result['extra']['prefill']['ms_per_call']:.3f} ms/call, "
+            f"{result['extra']['prefill']['achieved_tflops']:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_positions} positions ...")
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_positions)

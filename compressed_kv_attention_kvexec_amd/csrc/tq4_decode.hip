@@ -13,20 +13,15 @@
 // with no per-key Hadamard and no float K/V outside registers and LDS.
 //
 // Work decomposition: grid (split, KV head, request); 8 wavefronts per
-// workgroup; a wavefront owns 32-key tiles of its workgroup's key range.
+// workgroup; a wavefront owns every 8th 32-key tile of its workgroup's range.
 // Per tile and wavefront (GQA group of G <= 16 query heads padded to 16):
 //   S^T[32 keys][16 heads] = K_tile . Q_rot^T   16 x v_mfma_f32_16x16x32_f16
-//   online softmax in base 2 (norms folded into scores and weights)
-//   O[16 heads][256] += P . V_tile               16 x v_mfma_f32_16x16x32_f16
-// K operands: lane (row r, group gq) loads 16 bytes = 4 words of key r; each
-// word (8 dims) is one MFMA A-operand slice.  V operands need 8 keys per lane
-// at one dim, so a lane loads word w of 8 keys and transposes the 8x8 nibble
-// block in registers (v_perm and bitfield inserts).  A nibble byte becomes two
-// fp16 centroid values through an LDS table of 256 entries replicated once per
-// lane (lane-private banks, conflict-free), addressed with one v_perm.
-// The workgroup's partial (max, sum, accumulator) goes to the workspace; the
-// last workgroup of a (request, KV head) combines the partials in fixed split
-// order, applies the inverse rotation and writes bf16.
+//   online softmax in base 2 (key norms in the scores, value norms in P)
+//   O^T[256][16 heads] += V_tile^T . P^T        16 x v_mfma_f32_16x16x32_f16
+// Operand layouts and the centroid table are described in tq4_tile.h.  The
+// workgroup merges its wavefronts in LDS; with several splits it leaves
+// (max, sum, accumulator) in the workspace and tq4_decode_combine_kernel merges
+// the splits in fixed order, applies the inverse rotation and writes bf16.
 #include <type_traits>
 
 #include "tq4_device.h"
