@@ -21,7 +21,8 @@ from ._binding import (TQ4_BF16, TQ4_F16, TQ4_F32, Tq4Error, check, header_funct
 __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_encode_pages",
            "tq4_attn_decode_workspace_size", "tq4_attn_decode", "tq4_attn_prefill_workspace_size",
            "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library",
-           "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill"]
+           "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill",
+           "tq4_attn_decode_append", "prepare_decode_append"]
 
 HEAD_DIM = 256
 WORDS = 32
@@ -116,7 +117,7 @@ def tq4_attn_prefill_workspace_size(prior_len: int, chunk_len: int, n_q_heads: i
 
 
 def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace buffer (the library keeps it zeroed where it must be)."""
+    """A workspace buffer of at least 256 bytes (the calls do not read its contents on entry)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
@@ -136,6 +137,27 @@ def tq4_attn_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tenso
         ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
         _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tq4_attn_decode_append(pool: Tq4LayerPool, k_new, v_new, new_slots: torch.Tensor, q: torch.Tensor,
+                           page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """Encode each request's new token (k_new / v_new [batch][n_kv][256] fp32 or bf16, written at
+    new_slots[b], the slot of position seq_lens[b] - 1) and attend, in one call."""
+    batch, n_q, _ = q.shape
+    src = k_new if k_new is not None else v_new
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                 pool.page_size), q.device)
+    ps = pool.struct()
+    check(load_library().tq4_attn_decode_append(
+        ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _dtype_code(src), _ptr(new_slots), _ptr(q), _dtype_code(q),
+        _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
@@ -200,3 +222,17 @@ def prepare_prefill(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tenso
             ctypes.c_float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream))
     return PreparedCall(load_library().tq4_attn_prefill_chunk, args, (ps, pool, q, page_table, out, workspace))
+
+
+def prepare_decode_append(pool: Tq4LayerPool, k_new, v_new, new_slots: torch.Tensor, q: torch.Tensor,
+                          page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                          out: torch.Tensor, workspace: torch.Tensor, stream=None) -> PreparedCall:
+    batch, n_q, _ = q.shape
+    src = k_new if k_new is not None else v_new
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _dtype_code(src), _ptr(new_slots), _ptr(q), _dtype_code(q),
+            _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len), n_q,
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return PreparedCall(load_library().tq4_attn_decode_append, args,
+                        (ps, pool, k_new, v_new, new_slots, q, page_table, seq_lens, out, workspace))

@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "tq4_device.h"
+#include "tq4_encode_wave.h"
 #include "tq4_launch.h"
 #include "tq4_tile.h"
 
@@ -36,6 +37,7 @@ constexpr int kMaxSplits = 256;
 constexpr int kPlanCUs = 256;       // MI355X compute units
 constexpr int kPlanWgsPerCU = 1;    // resident decode workgroups per CU
 constexpr int kMinTilesPerWave = 2;
+constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running maximum is moved
 
 struct DecodeArgs {
     DecodeParams p;
@@ -45,6 +47,7 @@ struct DecodeArgs {
     int32_t partial_floats;
     uint64_t parts_off;   // byte offset of the partials inside the workspace
     uint32_t lut_pairs[8];  // fp16 bits of 16 * centroid[i], two per word (i = 2k, 2k+1)
+    float thr[15];          // encoder thresholds (append path)
 };
 
 // ---------------------------------------------------------------- planning
@@ -79,6 +82,7 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
     __shared__ float head_f[16];
     __shared__ float resM[16];
     __shared__ float resL[16];
+    __shared__ int32_t progress[kDecWaves];  // tiles each wavefront has started
 
     const DecodeParams &p = a.p;
     const int G = a.group;
@@ -86,29 +90,20 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
 
-    int L = p.seq_lens[b];
-    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-    const int split_keys = a.split_tiles * kTile;
-    const int n_active = (L + split_keys - 1) / split_keys;
-    uint16_t *outp = p.out + (static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G) * kDim;
-    if (s >= n_active) {
-        if (L == 0 && s == 0)
-            for (int i = tid; i < G * kDim; i += kDecThreads) outp[i] = 0;
-        return;
-    }
-    const int key_begin = s * split_keys;
-    const int key_end = min(key_begin + split_keys, L);
-    const int n_tiles = (key_end - key_begin + kTile - 1) / kTile;
-
-    // ---- page IDs of this wave's tiles, 64 at a time in one VGPR (lane i: i-th tile of the chunk)
+    const int L_req = p.seq_lens[b];  // scalar load, requested first; used after the tile issue
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int n_mine = wave_u < n_tiles ? (n_tiles - wave_u + kDecWaves - 1) / kDecWaves : 0;
+    const int split_keys = a.split_tiles * kTile;
+    const int key_begin = s * split_keys;
     const int32_t *pt_row = p.page_table + static_cast<int64_t>(b) * p.table_stride;
+    const bool append_mode = p.k_new != nullptr || p.v_new != nullptr;
+
+    // ---- page IDs of this wave's tiles, 64 at a time in one VGPR (lane i: i-th tile of the
+    // chunk).  The table index is clamped into the row, so the load never depends on the
+    // request's length and can fly alongside it; entries past the length are never used.
     int pid_vec = 0;
     auto fetch_pids = [&](int chunk) {
-        const int j = chunk * kWave + lane;
-        const int tile = wave_u + j * kDecWaves;
-        pid_vec = (j < n_mine) ? pt_row[(key_begin + tile * kTile) / p.page_size] : 0;
+        const int tile = wave_u + (chunk * kWave + lane) * kDecWaves;
+        pid_vec = pt_row[min((key_begin + tile * kTile) / p.page_size, p.table_stride - 1)];
     };
     auto pid_of = [&](int j) -> int { return __builtin_amdgcn_readlane(pid_vec, j & (kWave - 1)); };
 
@@ -118,27 +113,55 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
         return tile_rec0(p, g, key0, pid_of(inext), valid_d);
     };
 
-    // ---- start streaming before any set-up work: the first tile's loads fly during the prologue
+    // One register set is refilled in place with the wavefront's next tile; a refill past the
+    // chunk's end is a dead load of one line (every lane at the pool's first record) that is
+    // never read.  It keeps every step's load count fixed, which keeps the compiler's wait counts
+    // exact.
     KRegs kr;
     VRegs vr;
-    bool valid_cur = false, valid_next = false;
-    int64_t rec_next = 0;
-    if (n_mine > 0) {
-        fetch_pids(0);
-        rec_next = rec_of(wave_u, 0, valid_next);
-        load_k(p, rec_next, lofs, kr);
-        load_v(p, rec_next, lofs, vr);
-    }
+    bool valid_t = false;
+    const LaneOffsets dead_ofs{0u, 0u, 0u};
+    auto issue = [&](int t, int inext, bool live) {
+        const int64_t rec = rec_of(t, inext, valid_t);
+        const int64_t r = live ? rec : 0;
+        const LaneOffsets o = live ? lofs : dead_ofs;
+        __builtin_amdgcn_sched_barrier(0);  // same issue order on every path into the loop
+        load_k(p, r, o, kr);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(p, r, o, vr);
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // ---- prologue: zero the query operand, fill the centroid table, rotate the group's queries
-    reinterpret_cast<u32x4 *>(&qop_sh[0][0])[tid] = u32x4{0u, 0u, 0u, 0u};  // 512 x 16 B
-    build_lut(lut_mem, a.lut_pairs, tid, kDecThreads);
-    __syncthreads();
-    for (int h = wave; h < G; h += kDecWaves) {
+    // ---- start streaming before anything else: the query row of this wavefront's first head
+    // (clamped: waves past the group load a valid row and ignore it), the page IDs and the first
+    // tile, all before the length is known.  A first tile past the length is a real but unused
+    // load of a valid record.  Every path issues exactly these loads in this order, so the
+    // compiler's wait counts stay exact through the prologue.
+    const int q_h0 = min(wave_u, G - 1);
+    const u32x2 q_raw0 = *reinterpret_cast<const u32x2 *>(
+        p.q + (static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G + q_h0) * kDim + 4 * lane);
+    fetch_pids(0);
+    issue(wave_u, 0, true);
+
+    const int L = L_req < 0 ? 0 : (L_req > p.max_seq_len ? p.max_seq_len : L_req);
+    const int n_active = (L + split_keys - 1) / split_keys;
+    uint16_t *outp = p.out + (static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G) * kDim;
+    if (s >= n_active) {
+        if (L == 0 && s == 0)
+            for (int i = tid; i < G * kDim; i += kDecThreads) outp[i] = 0;
+        return;
+    }
+    const int key_end = min(key_begin + split_keys, L);
+    const int n_tiles = (key_end - key_begin + kTile - 1) / kTile;
+    const int n_mine = wave_u < n_tiles ? (n_tiles - wave_u + kDecWaves - 1) / kDecWaves : 0;
+
+    // ---- prologue: fill the centroid table and the rotated-query operand (each column written
+    // once: query heads by their wavefront, padding columns zeroed), one barrier
+    build_lut<kDecThreads>(lut_mem, a.lut_pairs, tid);
+    if (tid < kDecWaves) progress[tid] = 0;
+    auto rotate_head = [&](int h, u32x2 raw) {
         // one wavefront rotates query head h: y = H q (unnormalised), then a power-of-two scale
         // puts max |y| in [2^13, 2^14) for the fp16 operand
-        const uint16_t *qh = p.q + ((static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G + h) * kDim);
-        const u32x2 raw = *reinterpret_cast<const u32x2 *>(qh + 4 * lane);
         float y[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
                       __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
         wave_fwht(y, lane);
@@ -156,8 +179,48 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
         hv.x = pack_f16x2(y[0] * qs, y[1] * qs);
         hv.y = pack_f16x2(y[2] * qs, y[3] * qs);
         *reinterpret_cast<u32x2 *>(reinterpret_cast<char *>(&qop_sh[ks][dst_lane]) + 8 * (lane & 1)) = hv;
-    }
+    };
+    auto zero_column = [&](int c) {  // 8 K-steps x 4 lane groups of 16 bytes
+        if (lane < 32) reinterpret_cast<u32x4 *>(&qop_sh[lane & 7][16 * (lane >> 3) + c])[0] = u32x4{0u, 0u, 0u, 0u};
+    };
+    if (wave_u < G)
+        rotate_head(wave_u, q_raw0);  // the row requested before the tiles
+    else
+        zero_column(wave_u);
+    if (wave_u + kDecWaves < G)  // groups of more than 8 heads
+        rotate_head(wave_u + kDecWaves,
+                    *reinterpret_cast<const u32x2 *>(p.q + (static_cast<int64_t>(b) * p.n_q +
+                                                            static_cast<int64_t>(g) * G + wave_u + kDecWaves) * kDim +
+                                                     4 * lane));
+    else
+        zero_column(wave_u + kDecWaves);
     __syncthreads();
+
+    // ---- append path: only the wavefront that owns the request's last tile ever loads it, so
+    // that wavefront writes the new token's K and V records (position seq_len - 1) here, before
+    // its loop; if its first tile, requested above, is that last tile, it requests it again.
+    if (append_mode && s == n_active - 1 && n_tiles > 0 && wave_u == (n_tiles - 1) % kDecWaves) {
+        const int slot = p.new_slots[b];
+        if (slot >= 0 && slot < p.num_pages * p.page_size) {
+            const int page = slot / p.page_size;
+            const int64_t rec = (static_cast<int64_t>(page) * p.n_kv + g) * p.page_size + (slot - page * p.page_size);
+            const size_t off = (static_cast<size_t>(b) * p.n_kv + g) * kDim * (p.new_bf16 ? 2 : 4);
+            float xk[4], xv[4];
+            if (p.k_new != nullptr) encode_load(static_cast<const char *>(p.k_new) + off, p.new_bf16 != 0, lane, xk);
+            if (p.v_new != nullptr) encode_load(static_cast<const char *>(p.v_new) + off, p.new_bf16 != 0, lane, xv);
+            if (p.k_new != nullptr)
+                encode_values(xk, a.thr, const_cast<uint32_t *>(p.k_words) + rec * kWords,
+                              const_cast<uint16_t *>(p.k_norms) + rec, lane);
+            if (p.v_new != nullptr)
+                encode_values(xv, a.thr, const_cast<uint32_t *>(p.v_words) + rec * kWords,
+                              const_cast<uint16_t *>(p.v_norms) + rec, lane);
+        }
+        // vmcnt(0): the record stores (and the stale first tile) have completed before the
+        // wavefront loads the last tile (vmcnt bits [3:0] and [15:14] zero, expcnt and lgkmcnt
+        // left at max)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (n_mine == 1) issue(wave_u, 0, true);
+    }
     const float fcol = (n < G) ? head_f[n] : 0.f;
     const char *lut = reinterpret_cast<const char *>(lut_mem);
     const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;
@@ -168,11 +231,21 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    // One tile per step, one register set refilled in place: the next tile's K is requested as
-    // soon as this tile's scores exist, its V as soon as this tile's P.V products are issued.
-    auto step = [&](int t, int inext, auto prefetch) {
+    // One tile per step, its register set refilled in place with tile t + 8: the next K is
+    // requested as soon as this tile's scores exist, the next V as soon as its P.V products are
+    // issued.  live == false makes the refill a dead load (past the chunk's end).
+    // Issue priority: the two wavefronts sharing a SIMD (w and w ^ 4) would otherwise be served
+    // oldest first, and the younger one would finish its equal share of tiles much later.  Each
+    // wavefront publishes how many tiles it has started; the younger one takes the higher
+    // priority while it is not ahead of its partner, the older one only while it is behind.
+    // Tile assignment stays static, so results do not depend on timing.
+    const int partner = wave_u ^ (kDecWaves / 2);
+    const bool younger = wave_u >= kDecWaves / 2;
+    auto step = [&](int t, int inext, bool live, int done) {
+        if (lane == 0) progress[wave_u] = done;
+        const int other = __builtin_amdgcn_readfirstlane(progress[partner]);
         const int key0 = key_begin + t * kTile;
-        const bool valid = valid_cur;
+        const bool valid = valid_t;
         // ---- scores S^T (rows: keys, columns: heads)
         float4v sacc[2];
 #pragma unroll
@@ -197,20 +270,27 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
                 sc[4 * h + r] = (koff < lim) ? sacc[h][r] * kn4[r] * fcol : -INFINITY;
             }
         }
-        if constexpr (decltype(prefetch)::value) {
-            rec_next = rec_of(t + kDecWaves, inext, valid_next);
-            __builtin_amdgcn_sched_barrier(0);
-            load_k(p, rec_next, lofs, kr);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        const int64_t rec = rec_of(t + kDecWaves, inext, valid_t);
+        const int64_t rec_pf = live ? rec : 0;
+        const LaneOffsets ofs_pf = live ? lofs : dead_ofs;
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(p, rec_pf, ofs_pf, kr);
+        __builtin_amdgcn_sched_barrier(0);
+        if (younger ? (done <= other) : (done < other))
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
         float mx = sc[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float m_new = fmaxf(m_run, mx);
-        // this lane's accumulators all belong to head n, so the rescale factor is lane-local
-        if (__any(m_new > m_run)) {  // rare once the running maxima settle
+        // The reference maximum moves only when a score exceeds it by more than kRescaleSlack
+        // (so exp2(s - m_run) <= 256, well inside fp16): the softmax does not depend on the
+        // reference, and rescaling the 64 accumulators becomes rare.  This lane's accumulators
+        // all belong to head n, so the rescale factor is lane-local.
+        if (__any(mx > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
             const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             l_run *= alpha;
 #pragma unroll
@@ -246,29 +326,22 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
             for (int i = 0; i < 8; ++i)
                 oacc[8 * c + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lut_decode(u[i], lane4, lut), pop, oacc[8 * c + i], 0, 0, 0);
         }
-        if constexpr (decltype(prefetch)::value) {
-            __builtin_amdgcn_sched_barrier(0);
-            load_v(p, rec_next, lofs, vr);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        valid_cur = valid_next;
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(p, rec_pf, ofs_pf, vr);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- main loop over chunks of 64 tiles; inside a chunk every load is unconditional (the
-    // chunk's last tile is peeled), which keeps the wait counters exact
+    // ---- main loop over chunks of 64 tiles (one VGPR of page IDs)
     for (int c0 = 0; c0 < n_mine; c0 += kWave) {
         const int cn = min(kWave, n_mine - c0);
         const int tc = wave_u + c0 * kDecWaves;  // first tile of the chunk
         if (c0 > 0) {
             fetch_pids(c0 / kWave);
-            rec_next = rec_of(tc, 0, valid_next);
-            load_k(p, rec_next, lofs, kr);
-            load_v(p, rec_next, lofs, vr);
+            issue(tc, 0, true);
         }
-        valid_cur = valid_next;
-        for (int i = 0; i + 1 < cn; ++i) step(tc + i * kDecWaves, i + 1, std::true_type{});
-        step(tc + (cn - 1) * kDecWaves, 0, std::false_type{});
+        for (int i = 0; i < cn; ++i) step(tc + i * kDecWaves, i + 1, i + 1 < cn, c0 + i);
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- per-wave softmax totals
     float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
@@ -280,68 +353,89 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // ---- combine the workgroup's waves (fixed order) into LDS: M, L, O[G][256]
-    float *scratch = reinterpret_cast<float *>(lut_mem);
-    float *obuf = scratch;                                 // [slots][G][256]
-    const int per_slot = G * kDim;
-    const int slots = (kLutWords - kDim * 16) / per_slot;  // the last 16 rows hold the result
-    float *res = scratch + kLutWords - kDim * 16;           // [G][256] combined accumulator
-    if (tid < G) {
+    // ---- merge the workgroup's waves.  Each lane rescales its accumulators (all of head n) to
+    // the workgroup maximum; then a fixed-order tree in LDS adds waves 4..7 into 0..3, 2..3 into
+    // 0..1 and 1 into 0.  The LDS image keeps the accumulator lane layout ([wave][register][lane]
+    // as 16-byte rows), so every access is conflict-free.
+    {
         float M = -INFINITY;
-        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, stat_m[w][tid]);
-        float Ls = 0.f;
-        for (int w = 0; w < kDecWaves; ++w)
-            Ls += (stat_m[w][tid] == -INFINITY) ? 0.f : stat_l[w][tid] * __builtin_amdgcn_exp2f(stat_m[w][tid] - M);
-        resM[tid] = M;
-        resL[tid] = Ls;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, stat_m[w][n]);
+        const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) oacc[tt] *= f;
+        if (tid < G) {
+            float Ls = 0.f;
+            for (int w = 0; w < kDecWaves; ++w)
+                Ls += (stat_m[w][tid] == -INFINITY) ? 0.f : stat_l[w][tid] * __builtin_amdgcn_exp2f(stat_m[w][tid] - M);
+            resM[tid] = M;
+            resL[tid] = Ls;
+        }
     }
-    __syncthreads();
-    for (int i = tid; i < per_slot; i += kDecThreads) res[i] = 0.f;
-    for (int w0 = 0; w0 < kDecWaves; w0 += slots) {
-        if (wave >= w0 && wave < w0 + slots) {
-            float *dst = obuf + (wave - w0) * per_slot;
-            if (n < G) {
-                const float mw = stat_m[wave][n];
-                const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - resM[n]);
+    float4v *tree = reinterpret_cast<float4v *>(lut_mem);  // [4][16][64] rows of 16 bytes = 64 KiB
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+    for (int half = kDecWaves / 2; half >= 1; half >>= 1) {
+        if (wave_u >= half && wave_u < 2 * half) {
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            dst[n * kDim + 8 * (2 * (4 * gq + r) + c) + i] = oacc[8 * c + i][r] * f;
-            }
+            for (int tt = 0; tt < 16; ++tt) tree[((wave_u - half) * 16 + tt) * kWave + lane] = oacc[tt];
         }
         __syncthreads();
-        const int cnt = min(slots, kDecWaves - w0);
-        for (int i = tid; i < per_slot; i += kDecThreads) {
-            float acc = res[i];
-            for (int w = 0; w < cnt; ++w) acc += obuf[w * per_slot + i];
-            res[i] = acc;
+        if (wave_u < half) {
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) oacc[tt] += tree[(wave_u * 16 + tt) * kWave + lane];
         }
         __syncthreads();
     }
 
     if (n_active > 1) {
-        // more than one split: leave (M, L, O) for the combine kernel
-        const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
-        float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
-                     (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
-        if (tid < G) {
-            dst[tid] = resM[tid];
-            dst[16 + tid] = resL[tid];
+        // more than one split: wave 0 leaves (M, L, O[G][256]) for the combine kernel; lane
+        // (gq, n) holds dims 8 (2 (4 gq + r) + c) + i of head n in oacc[8 c + i][r]
+        if (wave_u == 0) {
+            const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
+            float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
+                         (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
+            if (lane < G) {
+                dst[lane] = resM[lane];
+                dst[16 + lane] = resL[lane];
+            }
+            if (n < G) {
+                float *row = dst + 32 + n * kDim;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const int d0 = 8 * (2 * (4 * gq + r) + c);
+                        *reinterpret_cast<float4 *>(row + d0) =
+                            make_float4(oacc[8 * c][r], oacc[8 * c + 1][r], oacc[8 * c + 2][r], oacc[8 * c + 3][r]);
+                        *reinterpret_cast<float4 *>(row + d0 + 4) =
+                            make_float4(oacc[8 * c + 4][r], oacc[8 * c + 5][r], oacc[8 * c + 6][r], oacc[8 * c + 7][r]);
+                    }
+            }
         }
-        float4 *d4 = reinterpret_cast<float4 *>(dst + 32);
-        const float4 *r4 = reinterpret_cast<const float4 *>(res);
-        for (int i = tid; i < G * (kDim / 4); i += kDecThreads) d4[i] = r4[i];
         return;
     }
 
-    // ---- single split: inverse rotation and output, o = H O / (256 L)
-    for (int h = wave; h < G; h += kDecWaves) {
-        float y[4];
+    // ---- single split: wave 0 writes O to LDS as [head][64 quads of dims], quads swizzled
+    // within groups of 8 so both this scatter and the row reads below spread over the banks;
+    // then one wave per head applies the inverse rotation, o = H O / (256 L)
+    auto quad_at = [](int h, int qd) { return h * 64 + (qd ^ ((h + 2 * (qd >> 4)) & 7)); };
+    float4v *res4 = tree;
+    if (wave_u == 0 && n < G) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = res[h * kDim + 4 * lane + r];
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int qd = 16 * gq + 4 * r + 2 * c + hf;
+                    res4[quad_at(n, qd)] = float4v{oacc[8 * c + 4 * hf][r], oacc[8 * c + 4 * hf + 1][r],
+                                                   oacc[8 * c + 4 * hf + 2][r], oacc[8 * c + 4 * hf + 3][r]};
+                }
+    }
+    __syncthreads();
+    for (int h = wave; h < G; h += kDecWaves) {
+        const float4v v = res4[quad_at(h, lane)];
+        float y[4] = {v[0], v[1], v[2], v[3]};
         wave_fwht(y, lane);
         const float Lh = resL[h];
         const float f = Lh > 0.f ? (1.0f / 256.0f) / Lh : 0.f;
@@ -441,6 +535,7 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStrea
     a.partial_floats = static_cast<int32_t>(plan.partial_floats);
     a.parts_off = plan.counters_bytes;
     lut_pairs_from_codebook(a.lut_pairs, codebook().centroid);
+    for (int i = 0; i < 15; ++i) a.thr[i] = codebook().threshold[i];
     hipLaunchKernelGGL(tq4_decode_kernel, dim3(plan.n_splits, p.n_kv, p.batch), dim3(kDecThreads), 0, stream, a);
     if (plan.n_splits > 1)
         hipLaunchKernelGGL(tq4_decode_combine_kernel, dim3(plan.group, p.n_kv, p.batch), dim3(kCombThreads), 0,

@@ -61,6 +61,11 @@ struct DecodeParams {
     float scale;
     uint16_t *out;  // bf16 bits [batch][n_q][256]
     void *workspace;
+    // optional: encode one new token per request before attending (NULL k_new and v_new: none)
+    const void *k_new;  // [batch][n_kv][256] fp32 or bf16
+    const void *v_new;
+    int32_t new_bf16;
+    const int32_t *new_slots;  // [batch]
 };
 
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStream_t stream);

@@ -142,7 +142,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
             qop[j][ks] = __builtin_bit_cast(half8, v);
         }
     }
-    build_lut(lut_mem, a.lut_pairs, tid, kPfThreads);
+    build_lut<kPfThreads>(lut_mem, a.lut_pairs, tid);
     __syncthreads();
     const char *lut = reinterpret_cast<const char *>(lut_mem);
     const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;

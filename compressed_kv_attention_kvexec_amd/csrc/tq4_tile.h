@@ -148,14 +148,43 @@ __device__ __forceinline__ void wave_fwht(float y[4], int lane) {
 
 
 // Fill the centroid table: entry e (a nibble pair) -> fp16x2 (16 c[e & 15], 16 c[e >> 4]), one
-// copy per lane so each 256-byte row holds one entry; written 16 bytes at a time.
-__device__ __forceinline__ void build_lut(uint32_t *lut_mem, const uint32_t lut_pairs[8], int tid, int nthreads) {
-    for (int i = tid; i < kLutWords / 4; i += nthreads) {
-        const int e = i >> 4;
-        const uint32_t lo = (lut_pairs[(e & 15) >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t hi = (lut_pairs[(e >> 4) >> 1] >> (16 * ((e >> 4) & 1))) & 0xffffu;
-        const uint32_t v = lo | (hi << 16);
-        reinterpret_cast<u32x4 *>(lut_mem)[i] = u32x4{v, v, v, v};
+// copy per lane so each 256-byte row holds one entry; written 16 bytes at a time, 16 per entry.
+// With NT threads (256, 512 or 1024), thread t writes entries e = (t >> 4) + (NT >> 4) k, so its
+// low nibble (t >> 4) & 15 never changes and its high nibble is (t >> 8) + (NT >> 8) k.  The pair
+// words are taken into scalar registers and picked by selects over named values: an indexed
+// read of the argument array would be a vector memory load, and waiting for it would also wait
+// for every tile load already in flight.
+template <int NT>
+__device__ __forceinline__ void build_lut(uint32_t *lut_mem, const uint32_t lut_pairs[8], int tid) {
+    static_assert(NT == 256 || NT == 512 || NT == 1024, "table fill assumes 256, 512 or 1024 threads");
+    uint32_t l[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) l[k] = __builtin_amdgcn_readfirstlane(lut_pairs[k]);
+    const uint32_t c_lo = (static_cast<uint32_t>(tid) >> 4) & 15u;
+    const uint32_t k0 = c_lo >> 1;  // select tree, once per thread
+    const uint32_t a0 = (k0 & 1) ? l[1] : l[0], a1 = (k0 & 1) ? l[3] : l[2];
+    const uint32_t a2 = (k0 & 1) ? l[5] : l[4], a3 = (k0 & 1) ? l[7] : l[6];
+    const uint32_t b0 = (k0 & 2) ? a1 : a0, b1 = (k0 & 2) ? a3 : a2;
+    const uint32_t w_lo = (k0 & 4) ? b1 : b0;
+    const uint32_t v_lo = (c_lo & 1) ? (w_lo >> 16) : (w_lo & 0xffffu);
+    const uint32_t t8 = static_cast<uint32_t>(tid) >> 8;  // 0 .. NT / 256 - 1
+#pragma unroll
+    for (int k = 0; k < kLutWords / 4 / NT; ++k) {
+        // high nibble c = t8 + (NT / 256) k: word c / 2 of the pair table, half c & 1
+        uint32_t w;
+        if constexpr (NT == 256) {
+            w = l[k >> 1];
+        } else {
+            const int base = (NT / 256) * k;  // even: t8 picks among words base / 2 ..
+            const uint32_t c = t8 + static_cast<uint32_t>(base);
+            w = l[base >> 1];
+#pragma unroll
+            for (int j = 1; j < NT / 512; ++j) w = ((c >> 1) == static_cast<uint32_t>((base >> 1) + j)) ? l[(base >> 1) + j] : w;
+        }
+        const uint32_t c = (NT == 256) ? static_cast<uint32_t>(k) : t8 + static_cast<uint32_t>((NT / 256) * k);
+        const uint32_t v_hi = (c & 1) ? (w >> 16) : (w & 0xffffu);
+        const uint32_t v = v_lo | (v_hi << 16);
+        reinterpret_cast<u32x4 *>(lut_mem)[tid + NT * k] = u32x4{v, v, v, v};
     }
 }
 

@@ -175,6 +175,29 @@ tq4_status tq4_attn_decode(const tq4_layer_pool *pool, const void *q, tq4_dtype 
                            int32_t n_q_heads, float scale, void *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * tq4_attn_decode_append -- the decode step of a model layer in one call: encode
+ * each request's new token and attend ([KVX]: the cache is written in TQ4 and
+ * read back by the attention that follows).  Results are bit-identical to
+ * tq4_encode_pages(pool, k_new, v_new, src_dtype, new_slots, batch) followed by
+ * tq4_attn_decode(...) with the other arguments, provided new_slots[b] is the
+ * slot of position seq_lens[b] - 1 of request b (the new token is the last
+ * cached position); a new slot that another position of the call also reads
+ * races.
+ *
+ *   k_new, v_new : device [batch][n_kv_heads][256] in src_dtype (TQ4_F32 or
+ *                  TQ4_BF16), 16-byte aligned; either may be NULL, not both.
+ *   new_slots    : device int32 [batch]; slots outside the pool are skipped,
+ *                  and so is every request whose clamped length is 0.
+ *   other arguments as for tq4_attn_decode (seq_lens count the new token).
+ */
+tq4_status tq4_attn_decode_append(const tq4_layer_pool *pool, const void *k_new, const void *v_new,
+                                  tq4_dtype src_dtype, const int32_t *new_slots, const void *q,
+                                  tq4_dtype q_dtype, const int32_t *page_table, int32_t page_table_stride,
+                                  const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                  int32_t n_q_heads, float scale, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace tq4_attn_prefill_chunk needs (0 for invalid sizes). */
 size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,
                                        int32_t n_kv_heads, int32_t page_size);

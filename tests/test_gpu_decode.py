@@ -146,3 +146,59 @@ def test_decode_full_212k_sampled_head():
 def test_decode_full_two_requests_shared_prefix_sampled_head():
     got, ref = _sampled_full_size("decode_2req_shared", g=1, layer=0)
     parity(got, ref, "2req head 1")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_append_equals_encode_then_decode(dtype):
+    """The fused append call writes the same records as tq4_encode_pages and returns the same bits
+    as tq4_attn_decode on the updated pool; a second call reuses the workspace."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    from _pools import from_device
+    w = synth.Workload(99, "append", "decode", 1, 64, 80, seq_lens=(1, 63, 64, 65, 2000, 777))
+    pool, table = oracle_pool(w)
+    q_t, _ = bf16_queries(w, 0, w.batch)
+    rng = np.random.default_rng(99)
+    new = rng.standard_normal((2, w.batch, w.n_kv, 256)).astype(np.float32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    k_new, v_new = (torch.from_numpy(new[i]).to(tdt).cuda().contiguous() for i in range(2))
+    last = np.array([table[b, (L - 1) // 64] * 64 + (L - 1) % 64 for b, L in enumerate(w.seq_lens)], np.int32)
+    slots = torch.from_numpy(last).cuda()
+    tab = torch.from_numpy(table).cuda()
+    seq = torch.tensor(w.seq_lens, dtype=torch.int32).cuda()
+    # reference: separate encode then decode on a copy
+    ref_pool = to_device(pool)
+    tq4.tq4_encode_pages(ref_pool, k_new, v_new, slots)
+    ref = tq4.tq4_attn_decode(ref_pool, q_t.cuda(), tab, seq, max(w.seq_lens), synth.SCALE)
+    fused_pool = to_device(pool)
+    ws = tq4.new_workspace(tq4.tq4_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv, 64))
+    for _ in range(2):
+        got = tq4.tq4_attn_decode_append(fused_pool, k_new, v_new, slots, q_t.cuda(), tab, seq,
+                                         max(w.seq_lens), synth.SCALE, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+    a, b = from_device(fused_pool), from_device(ref_pool)
+    for x, y in ((a.k_words, b.k_words), (a.k_norms, b.k_norms), (a.v_words, b.v_words), (a.v_norms, b.v_norms)):
+        np.testing.assert_array_equal(x, y)
+    # and the new records are the oracle's
+    chk = oracle.Pool(pool.k_words.copy(), pool.k_norms.copy(), pool.v_words.copy(), pool.v_norms.copy())
+    oracle.encode_to_pool(chk, np.asarray(k_new.float().cpu()), np.asarray(v_new.float().cpu()), last)
+    np.testing.assert_array_equal(a.k_words, chk.k_words)
+    np.testing.assert_array_equal(a.v_norms, chk.v_norms)
+
+
+def test_decode_workspace_reuse_across_pools():
+    """One workspace serves consecutive calls on different pools and lengths (as the layers of a
+    decode step do); every call matches the oracle."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    ws = tq4.new_workspace(tq4.tq4_attn_decode_workspace_size(2, 9000, 24, 4, 64))
+    for layer, lens in enumerate([(9000, 4100), (300, 8999), (4096, 1)]):
+        w = synth.Workload(100, "reuse", "decode", 1, 64, 300, seq_lens=lens)
+        pool, table = oracle_pool(w, layer=layer)
+        q_t, q64 = bf16_queries(w, layer, w.batch)
+        got = tq4.tq4_attn_decode(to_device(pool), q_t.cuda(), torch.from_numpy(table).cuda(),
+                                  torch.tensor(lens, dtype=torch.int32).cuda(), max(lens), synth.SCALE,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        parity(got.cpu(), oracle.attn_decode(pool, q64, table, lens, synth.SCALE), f"reuse {lens}")
