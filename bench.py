@@ -220,6 +220,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-positions", type=int, default=131072)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager per-layer launches instead of a HIP graph of the step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -275,18 +277,51 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
+    # The step as one HIP graph: the same 16 calls (32 kernels) captured on a side stream and
+    # replayed, which removes the host launch gaps between them.
+    graph = None
+    if not args.no_graph:
+        gstream = torch.cuda.Stream()
+        gcalls = [tq4.prepare_decode_append(L["pool"], L["k_new"], L["v_new"], L["slot_new"], L["q"], L["table"],
+                                            L["seq"], max(w.seq_lens), synth.SCALE, outs[i], workspace, gstream)
+                  for i, L in enumerate(layers)]
+        try:
+            gstream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(gstream):
+                for c in gcalls:  # one eager pass on the capture stream first
+                    c()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=gstream):
+                for c in gcalls:
+                    c()
+            for _ in range(args.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            log(f"captured the step as a HIP graph; {args.warmup} warmup replays done")
+        except Exception as exc:  # capture unsupported: fall back to the eager step
+            log(f"graph capture failed ({exc}); timing the eager step")
+            graph = None
+
+    def timed_steps(run_step):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            run_step(k)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    elapsed_graph = timed_steps(lambda k: graph.replay()) if graph is not None else None
+    # eager steps with per-call events on every EVENT_EVERY-th layer: the decode call duration
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in timed_layers] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_eager = timed_steps(lambda k: step(ev[k]))
     dec_ms = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
     avg_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
-    log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.3f} ms/step, "
-        f"decode kernel avg {avg_dec_s * 1e6:.1f} us")
+    elapsed = elapsed_graph if elapsed_graph is not None else elapsed_eager
+    log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.3f} ms/step"
+        f"{' (graph)' if elapsed_graph is not None else ''}, eager {elapsed_eager * 1e3 / args.steps:.3f} ms/step, "
+        f"decode call avg {avg_dec_s * 1e6:.1f} us")
 
     # outputs must be finite (a cheap guard that the timed work produced results)
     for o in outs:
@@ -314,8 +349,11 @@ def main() -> int:
                      "kernel": "tq4_attn_decode_append call = tq4_decode_kernel + tq4_decode_combine_kernel",
                      "bytes_per_launch": bytes_launch, "avg_launch_us": avg_dec_s * 1e6},
         "extra": {"step_hbm_gb_per_s": step_gbs, "step_frac_of_peak": step_gbs / HBM_PEAK_GBS,
+                  "execution": "hip graph of the step's 16 calls" if elapsed_graph is not None else "eager launches",
+                  "eager_ms_per_step": elapsed_eager * 1e3 / args.steps,
+                  "eager_positions_per_s": positions / (elapsed_eager / args.steps),
                   "decode_calls_timed": len(dec_ms),
-                  "timed_calls": f"layers {timed_layers} of every timed step (events bracket each)"},
+                  "timed_calls": f"layers {timed_layers} of every eager timed step (events bracket each)"},
     }
     if build_stats.get("encode_seconds"):
         vps = build_stats["encode_vectors"] / build_stats["encode_seconds"]
@@ -323,7 +361,7 @@ def main() -> int:
         result["extra"]["encode"] = {"vectors_per_s": vps, "gb_per_s": vps * (1024 + 130) / 1e9,
                                      "frac_of_hbm_peak": vps * (1024 + 130) / 1e9 / HBM_PEAK_GBS,
                                      "sample": "pool build of layer 0 (K and V), 32,768-token launches"}
-    del layers, calls, outs, workspace
+    del layers, calls, outs, workspace, graph
     torch.cuda.empty_cache()
     ceiling = hbm_read_ceiling(dev)
     result["extra"]["hbm_read_ceiling_gb_per_s"] = ceiling

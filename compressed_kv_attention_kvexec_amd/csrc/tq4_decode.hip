@@ -448,76 +448,98 @@ __global__ __launch_bounds__(kDecThreads) void tq4_decode_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- combine kernel
 //
-// One workgroup per (query head, KV head, request): merges the split partials of that head in
-// fixed split order (max-rescaled sums), applies the inverse rotation and writes bf16.
+// One workgroup of four wavefronts per (query head, KV head, request) merges the split partials
+// of that head: every wavefront reduces the splits' maxima in registers (lane i holds split
+// 64 c + i), then wavefront w sums splits w, w + 4, ... for dims 4 l .. 4 l + 3 in lane l (16-byte
+// loads), and wavefront 0 adds the four sums in fixed order, applies the inverse rotation and
+// writes bf16.
 
-constexpr int kCombQuarters = 4;
-constexpr int kCombThreads = kDim * kCombQuarters;
+constexpr int kCombWaves = 4;
+constexpr int kCombThreads = kCombWaves * kWave;
+constexpr int kCombPerWave = kWave / kCombWaves;  // splits per wavefront in each group of 64
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
 
 __global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(DecodeArgs a) {
-    __shared__ float wgt[kMaxSplits];
-    __shared__ float sL[kMaxSplits];
-    __shared__ float part[kCombQuarters][kDim];
+    __shared__ float4v part[kCombWaves][kWave];
     const DecodeParams &p = a.p;
     const int G = a.group;
     const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, d = tid & (kDim - 1), qtr = tid / kDim;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int L_req = p.seq_lens[b];
     const size_t pf = static_cast<size_t>(a.partial_floats);
     const float *base = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + a.parts_off) +
                         (static_cast<size_t>(b) * p.n_kv + g) * a.n_splits * pf;
-    // Every load is issued before the sequence length is known: slots past the live splits hold
-    // stale data, so they are dropped by selection below, never multiplied in.
     const int ns = a.n_splits;
-    float m_k = -INFINITY, l_k = 0.f;
-    if (tid < ns) {
-        m_k = base[tid * pf + h];
-        l_k = base[tid * pf + 16 + h];
-    }
-    const float *col = base + 32 + h * kDim + d;
-    float v[16];
+    // Every load of the first group of 64 splits is issued before the length is known (slots past
+    // the live splits hold stale data and are dropped by selection, never multiplied in).
+    const int s_l = min(lane, ns - 1);
+    const float m0 = base[s_l * pf + h];
+    const float l0 = base[s_l * pf + 16 + h];
+    float4v v[kCombPerWave];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int k = qtr + kCombQuarters * u;
-        v[u] = k < ns ? col[k * pf] : 0.f;
+    for (int u = 0; u < kCombPerWave; ++u) {
+        const int s = min(wave + kCombWaves * u, ns - 1);
+        v[u] = *reinterpret_cast<const float4v *>(base + s * pf + 32 + h * kDim + 4 * lane);
     }
-    int L = p.seq_lens[b];
-    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    const int L = L_req < 0 ? 0 : (L_req > p.max_seq_len ? p.max_seq_len : L_req);
     const int split_keys = a.split_tiles * kTile;
     const int n_active = (L + split_keys - 1) / split_keys;
-    if (n_active <= 1) return;  // the split kernel wrote this output itself
-    if (tid < n_active) {
-        wgt[tid] = m_k;
-        sL[tid] = l_k;
+    // With one live split the split kernel wrote this output itself; such a request still runs
+    // the (harmless, in-bounds) arithmetic below but stores nothing.  An early return here would
+    // let the compiler sink the loads above behind the length's own load.
+    const bool merge = n_active > 1;
+    const int n_groups = (n_active + kWave - 1) / kWave;
+
+    // maximum over the live splits' reference maxima
+    float mx = lane < n_active ? m0 : -INFINITY;
+    for (int c = 1; c < n_groups; ++c) {
+        const int s = c * kWave + lane;
+        if (s < n_active) mx = fmaxf(mx, base[s * pf + h]);
     }
-    __syncthreads();
-    float M = -INFINITY;
-    for (int k = 0; k < n_active; ++k) M = fmaxf(M, wgt[k]);
-    __syncthreads();
-    if (tid < n_active) wgt[tid] = (m_k == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_k - M);
-    __syncthreads();
-    float acc = 0.f;
+    const float M = wave_max(mx);
+
+    auto weight = [&](float m) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M); };
+    float w_l = lane < n_active ? weight(m0) : 0.f;  // lane i: weight of split i
+    float lsum = lane < n_active ? w_l * l0 : 0.f;
+    float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int k = qtr + kCombQuarters * u;
-        acc += (k < n_active) ? wgt[k] * v[u] : 0.f;
+    for (int u = 0; u < kCombPerWave; ++u) {
+        const int s = wave + kCombWaves * u;
+        if (s < n_active) acc += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), s)) * v[u];
     }
-    for (int k = qtr + kCombQuarters * 16; k < n_active; k += kCombQuarters) acc += wgt[k] * col[k * pf];
-    part[qtr][d] = acc;
-    __syncthreads();
-    if (tid < kWave) {
-        // wavefront 0: sum the quarters, total weight, inverse rotation in registers, output
-        const int lane = tid;
-        float y[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int dd = 4 * lane + r;
-            y[r] = ((part[0][dd] + part[1][dd]) + part[2][dd]) + part[3][dd];
+    for (int c = 1; c < n_groups; ++c) {  // more than 64 splits
+        const int s = c * kWave + lane;
+        const float mc = s < n_active ? base[s * pf + h] : -INFINITY;
+        const float wc = s < n_active ? weight(mc) : 0.f;
+        lsum += s < n_active ? wc * base[s * pf + 16 + h] : 0.f;
+        for (int u = 0; u < kCombPerWave; ++u) {
+            const int s2 = c * kWave + wave + kCombWaves * u;
+            if (s2 < n_active) {
+                const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wc), wave + kCombWaves * u));
+                acc += ws * *reinterpret_cast<const float4v *>(base + s2 * pf + 32 + h * kDim + 4 * lane);
+            }
         }
-        float t = 0.f;
-        for (int k = lane; k < n_active; k += kWave) t += wgt[k] * sL[k];
-        for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, kWave);
+    }
+    const float Ltot = wave_sum(lsum);
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && merge) {
+        const float4v t = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        float y[4] = {t[0], t[1], t[2], t[3]};
         wave_fwht(y, lane);
-        const float f = t > 0.f ? (1.0f / 256.0f) / t : 0.f;
+        const float f = Ltot > 0.f ? (1.0f / 256.0f) / Ltot : 0.f;
         u32x2 o;
         o.x = static_cast<uint32_t>(f32_to_bf16(y[0] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[1] * f)) << 16);
         o.y = static_cast<uint32_t>(f32_to_bf16(y[2] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[3] * f)) << 16);
