@@ -46,4 +46,60 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Value of lane (lane ^ M) of a wavefront, M in {1, 2, 4, 8, 16, 32}, without the LDS crossbar:
+// DPP quad permutes for 1 and 2, DPP row rotates by 4 / 12 and 8 inside each 16-lane row for 4
+// and 8, and the lane-swap instructions between 16-lane rows and between 32-lane halves for 16
+// and 32.  (Both swap results are kept: each holds the partner's value in half of the lanes.)
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+    const int v = static_cast<int>(x);
+    if constexpr (M == 1) {
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    } else if constexpr (M == 2) {
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    } else if constexpr (M == 4) {
+        // banks 0 and 2 of each row (lanes 0-3, 8-11) read lane + 4 (row_ror:12), banks 1 and 3
+        // read lane - 4 (row_ror:4); the bank masks make the two moves write disjoint lanes
+        const int down = __builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0x5, false);
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(down, v, 0x124, 0xF, 0xA, false));
+    } else if constexpr (M == 8) {
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return static_cast<uint32_t>((lane & 16) ? r[0] : r[1]);
+    } else {
+        static_assert(M == 32, "lane_xor: M must be a power of two below 64");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return static_cast<uint32_t>((lane & 32) ? r[0] : r[1]);
+    }
+}
+
+template <int M>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+    return __builtin_bit_cast(float, lane_xor<M>(__builtin_bit_cast(uint32_t, x), lane));
+}
+
+// For M = 16 or 32: the pair (lo, hi) with lo = the value of the lower lane of each (l, l ^ M)
+// pair and hi = the value of the upper lane, in every lane (one swap instruction, no select).
+template <int M>
+__device__ __forceinline__ void lane_pair(float x, float &lo, float &hi) {
+    static_assert(M == 16 || M == 32, "lane_pair: M is 16 or 32");
+    // The elements are copied to plain ints before the bit casts: this compiler lowers
+    // __builtin_bit_cast of an element of a vector-typed value as a load from the vector's first
+    // element, which would make hi a copy of lo.
+    const int v = __builtin_bit_cast(int, x);
+    int r0, r1;
+    if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    }
+    lo = __builtin_bit_cast(float, r0);
+    hi = __builtin_bit_cast(float, r1);
+}
+
 }  // namespace tq4

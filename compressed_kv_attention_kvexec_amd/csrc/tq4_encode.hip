@@ -20,31 +20,79 @@ struct EncodeArgs {
     float thr[15];
 };
 
-__global__ __launch_bounds__(256) void tq4_encode_kernel(EncodeArgs a) {
+constexpr int kEncWaves = 4;               // wavefronts per workgroup
+constexpr int64_t kEncMaxWorkgroups = 2048;  // 8 per CU (all resident): each wavefront loops over vectors
+constexpr int kEncDropOffset = 0x40000000;   // a buffer offset past any record: the store is dropped
+constexpr int kBufferFlags = 0x00020000;     // raw 32-bit buffer resource word 3
+
+// Each wavefront encodes vectors wave0, wave0 + stride, ... ([half][token][kv head] order).  The
+// loop body has no branches: the next vector's source and slot are requested (index clamped)
+// before the current vector is encoded, and the record is written through buffer resources that
+// cover exactly the record (or nothing, for a slot outside the pool), so lanes that must not
+// store and invalid slots are dropped by the hardware.  With no branch around loads or stores
+// the compiler's wait counts stay exact: each iteration waits only for its own source.
+template <bool BF16>
+__global__ __launch_bounds__(kEncWaves * kWave) void tq4_encode_kernel(EncodeArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int64_t per_half = static_cast<int64_t>(a.p.n_tokens) * a.p.n_kv;
-    // vectors are ordered [half][token][kv head]; halves with no source are not launched
-    int half;
-    int64_t rem;
-    if (a.p.src[0] != nullptr) {
-        half = vec < per_half ? 0 : 1;
-        rem = vec - half * per_half;
-    } else {
-        half = 1;
-        rem = vec;
+    // vector indices fit in 31 bits (the launch checks it)
+    const int wave0 = static_cast<int>(blockIdx.x) * kEncWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int stride = static_cast<int>(gridDim.x) * kEncWaves;
+    const int per_half = a.p.n_tokens * a.p.n_kv;
+    const int first_half = a.p.src[0] != nullptr ? 0 : 1;
+    const int total = per_half * ((a.p.src[0] != nullptr) + (a.p.src[1] != nullptr));
+    if (wave0 >= total) return;
+    constexpr size_t esize = BF16 ? 2 : 4;
+    auto half_of = [&](int vec) { return first_half + static_cast<int>(vec >= per_half); };
+    auto rem_of = [&](int vec) { return vec - (vec >= per_half ? per_half : 0); };
+    auto load = [&](int vec, float x[4], int &slot) {
+        const int rem = rem_of(vec);
+        encode_load(static_cast<const char *>(a.p.src[half_of(vec)]) + static_cast<int64_t>(rem) * kDim * esize, BF16,
+                    lane, x);
+        slot = a.p.slots[rem / a.p.n_kv];
+    };
+    const int word_off = (lane & 1) ? kEncDropOffset : (lane >> 1) * 4;
+    const int norm_off = lane == 0 ? 0 : kEncDropOffset;
+
+    // encode vector vec from x (slot = its page-table slot) and write its record; live == false
+    // (a clamped repeat of a vector past the end) drops both stores
+    auto encode_store = [&](int vec, const float x[4], int slot, bool live) {
+        const int half = half_of(vec);
+        const int head = rem_of(vec) % a.p.n_kv;
+        const int s_u = __builtin_amdgcn_readfirstlane(slot);
+        const bool valid = live && s_u >= 0 && s_u < a.p.num_slots;
+        const int sl = valid ? s_u : 0;
+        const int page = sl / a.p.page_size;
+        const int64_t rec = (static_cast<int64_t>(page) * a.p.n_kv + head) * a.p.page_size + (sl - page * a.p.page_size);
+        uint32_t word;
+        const float n32 = encode_compute(x, a.thr, lane, word);
+        const __amdgpu_buffer_rsrc_t wr =
+            __builtin_amdgcn_make_buffer_rsrc(a.p.words[half] + rec * kWords, 0, valid ? kWords * 4 : 0, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t nr =
+            __builtin_amdgcn_make_buffer_rsrc(a.p.norms[half] + rec, 0, valid ? 2 : 0, kBufferFlags);
+        __builtin_amdgcn_raw_buffer_store_b32(word, wr, word_off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_f16_bits(n32), nr, norm_off, 0, 0);
+    };
+
+    // two register sets used in turn (no copies between iterations)
+    float x0[4], x1[4];
+    int slot0, slot1;
+    load(wave0, x0, slot0);
+    {   // two dropped stores: the loop is entered with the same pending operations as its back edge
+        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.p.words[half_of(wave0)], 0, 0, kBufferFlags);
+        __builtin_amdgcn_raw_buffer_store_b32(0u, none, word_off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), none, norm_off, 0, 0);
     }
-    if (rem >= per_half || a.p.src[half] == nullptr) return;
-    const int token = static_cast<int>(rem / a.p.n_kv);
-    const int head = static_cast<int>(rem % a.p.n_kv);
-    const int slot = a.p.slots[token];
-    if (slot < 0 || slot >= a.p.num_slots) return;
-    const int page = slot / a.p.page_size;
-    const int off = slot - page * a.p.page_size;
-    const int64_t rec = (static_cast<int64_t>(page) * a.p.n_kv + head) * a.p.page_size + off;
-    const size_t esize = a.p.src_bf16 ? 2 : 4;
-    encode_vector_wave(static_cast<const char *>(a.p.src[half]) + rem * kDim * esize, a.p.src_bf16 != 0, a.thr,
-                       a.p.words[half] + rec * kWords, a.p.norms[half] + rec, lane);
+    for (int vec = wave0; vec < total; vec += 2 * stride) {
+        const bool live1 = vec < total - stride;
+        const int v1 = live1 ? vec + stride : vec;
+        load(v1, x1, slot1);
+        __builtin_amdgcn_sched_barrier(0);  // requested before this vector's work
+        encode_store(vec, x0, slot0, true);
+        const int v2 = vec < total - 2 * stride ? vec + 2 * stride : vec;
+        load(v2, x0, slot0);
+        __builtin_amdgcn_sched_barrier(0);
+        encode_store(v1, x1, slot1, live1);
+    }
 }
 
 hipError_t launch_encode(const EncodeParams &p, hipStream_t stream) {
@@ -55,9 +103,13 @@ hipError_t launch_encode(const EncodeParams &p, hipStream_t stream) {
     const int halves = (p.src[0] != nullptr) + (p.src[1] != nullptr);
     const int64_t vectors = static_cast<int64_t>(halves) * p.n_tokens * p.n_kv;
     if (vectors == 0) return hipSuccess;
-    const int64_t blocks = (vectors + 3) / 4;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(tq4_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a);
+    if (vectors > 0x7fffffff - 2 * kEncMaxWorkgroups * kEncWaves) return hipErrorInvalidValue;
+    int64_t blocks = (vectors + kEncWaves - 1) / kEncWaves;
+    if (blocks > kEncMaxWorkgroups) blocks = kEncMaxWorkgroups;
+    if (p.src_bf16)
+        hipLaunchKernelGGL(tq4_encode_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kEncWaves * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL(tq4_encode_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kEncWaves * kWave), 0, stream, a);
     return hipGetLastError();
 }
 

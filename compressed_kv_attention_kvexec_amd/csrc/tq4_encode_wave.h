@@ -16,8 +16,6 @@
 
 namespace tq4 {
 
-__device__ __forceinline__ float enc_xor_lane(float v, int mask) { return __shfl_xor(v, mask, kWave); }
-
 // Lane l's four source values (dims 4l .. 4l+3) of a 256-dim fp32 or bf16 vector.
 __device__ __forceinline__ void encode_load(const void *src, bool bf16, int lane, float x[4]) {
     if (bf16) {
@@ -37,9 +35,46 @@ __device__ __forceinline__ void encode_load(const void *src, bool bf16, int lane
     }
 }
 
-// Encodes the vector whose lane values encode_load returned; writes 32 words and the fp16 norm.
-__device__ __forceinline__ void encode_values(const float x[4], const float thr[15], uint32_t *words,
-                                              uint16_t *norm, int lane) {
+// Both halves of a butterfly in one add: lanes in the upper half of a pair compute
+// other + (-y), which is the same IEEE operation as other - y; lanes in the lower half compute
+// other + y, equal to y + other.
+__device__ __forceinline__ float flip_if(float y, bool upper) {
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, y) ^ (upper ? 0x80000000u : 0u));
+}
+
+template <int M>
+__device__ __forceinline__ void enc_stage(float y[4], int lane) {  // Hadamard stage h = 4 M
+    const bool upper = (lane & M) != 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (M >= 16) {
+            // lower lane: lo + hi; upper lane: lo - hi = lo + (-hi)
+            float lo, hi;
+            lane_pair<M>(y[r], lo, hi);
+            y[r] = lo + flip_if(hi, upper);
+        } else {
+            y[r] = lane_xor<M>(y[r], lane) + flip_if(y[r], upper);
+        }
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void norm_stage(float s[4], int lane) {  // tree strides 4 M
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (M >= 16) {
+            float lo, hi;
+            lane_pair<M>(s[r], lo, hi);
+            s[r] = lo + hi;  // both lanes of a pair: s[i] + s[i + stride]
+        } else {
+            s[r] = s[r] + lane_xor<M>(s[r], lane);
+        }
+    }
+}
+
+// Encodes the vector whose lane values encode_load returned: returns the fp32 norm and sets
+// word = the packed word (8 indices) that even lane 2k stores as word k.
+__device__ __forceinline__ float encode_compute(const float x[4], const float thr[15], int lane, uint32_t &word) {
 #pragma clang fp contract(off)
     // ---- squared norm: strides 128 .. 4 are lane strides 32 .. 1, then 2 and 1 in registers.
     // Pairing element e with e ^ stride on every lane reproduces the tree, since fp32 addition
@@ -47,11 +82,12 @@ __device__ __forceinline__ void encode_values(const float x[4], const float thr[
     float s[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[r] = x[r] * x[r];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = s[r] + enc_xor_lane(s[r], m);
-    }
+    norm_stage<32>(s, lane);
+    norm_stage<16>(s, lane);
+    norm_stage<8>(s, lane);
+    norm_stage<4>(s, lane);
+    norm_stage<2>(s, lane);
+    norm_stage<1>(s, lane);
     s[0] = s[0] + s[2];
     s[1] = s[1] + s[3];
     s[0] = s[0] + s[1];
@@ -66,30 +102,47 @@ __device__ __forceinline__ void encode_values(const float x[4], const float thr[
         y[1] = t1 + t3;
         y[3] = t1 - t3;
     }
-#pragma unroll
-    for (int m = 1; m <= 32; m <<= 1) {  // h = 4 m
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float other = enc_xor_lane(y[r], m);
-            y[r] = upper ? (other - y[r]) : (y[r] + other);
-        }
-    }
+    enc_stage<1>(y, lane);
+    enc_stage<2>(y, lane);
+    enc_stage<4>(y, lane);
+    enc_stage<8>(y, lane);
+    enc_stage<16>(y, lane);
+    enc_stage<32>(y, lane);
 
-    // ---- thresholds and indices
+    // ---- thresholds and indices.  idx = #{ i : y > t_i }, t_i = b_i * (16 n).  The thresholds
+    // are exact negatives of each other (b_14-i = -b_i, b_7 = 0), so with a = |y|:
+    //   y > 0:  idx = 8 + #{ j >= 8 : a > t_j }
+    //   y <= 0: idx = #{ j >= 8 : a < t_j } = 7 - #{ j >= 8 : a >= t_j },
+    // and a >= t is a' > t for a' the next float above a.
     const float mscale = 16.0f * n32;
-    uint32_t idx[4] = {0u, 0u, 0u, 0u};
+    float t[7];
 #pragma unroll
-    for (int i = 0; i < 15; ++i) {
-        const float t = thr[i] * mscale;
+    for (int j = 0; j < 7; ++j) t[j] = thr[8 + j] * mscale;
+    uint32_t idx[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) idx[r] += (y[r] > t) ? 1u : 0u;
+    for (int r = 0; r < 4; ++r) {
+        const bool pos = y[r] > 0.0f;
+        const uint32_t abits = __builtin_bit_cast(uint32_t, y[r]) & 0x7fffffffu;
+        const float a = __builtin_bit_cast(float, pos ? abits : abits + 1u);
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < 7; ++j) c += (a > t[j]) ? 1u : 0u;
+        idx[r] = pos ? 8u + c : 7u - c;
     }
 
     // ---- pack: lanes 2k and 2k+1 hold dims 8k .. 8k+7
     const uint32_t half16 = idx[0] | (idx[1] << 4) | (idx[2] << 8) | (idx[3] << 12);
-    const uint32_t other16 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(half16), 1, kWave));
-    if ((lane & 1) == 0) words[lane >> 1] = half16 | (other16 << 16);
+    const uint32_t other16 = lane_xor<1>(half16, lane);
+    word = half16 | (other16 << 16);
+    return n32;
+}
+
+// Encodes the vector whose lane values encode_load returned; writes 32 words and the fp16 norm.
+__device__ __forceinline__ void encode_values(const float x[4], const float thr[15], uint32_t *words,
+                                              uint16_t *norm, int lane) {
+    uint32_t word;
+    const float n32 = encode_compute(x, thr, lane, word);
+    if ((lane & 1) == 0) words[lane >> 1] = word;
     if (lane == 0) *norm = f32_to_f16_bits(n32);
 }
 
