@@ -194,9 +194,9 @@ def prefill_leg(device, reps: int = 3):
             "query_tokens_per_s": w.chunk_len / (ms / 1e3), "calls_timed": reps}
 
 
-def hbm_read_ceiling(device, gib: int = 4, reps: int = 5) -> float:
-    """Achievable HBM read bandwidth on this GPU: a plain fp32 sum over `gib` GiB (far beyond the
-    256 MB Infinity Cache), GB/s, best of `reps`."""
+def torch_sum_read(device, gib: int = 4, reps: int = 5) -> float:
+    """Read rate of torch's fp32 sum over `gib` GiB (far beyond the 256 MB Infinity Cache), GB/s,
+    best of `reps`: what a library reduction kernel reads, below the hardware's streaming ceiling."""
     import torch
     x = torch.ones(gib * (1 << 30) // 4, dtype=torch.float32, device=device)
     x.sum()
@@ -389,10 +389,11 @@ def main() -> int:
         f"{result['extra']['encode']['gb_per_s']:.0f} GB/s")
     del layers, calls, outs, workspace, graph
     torch.cuda.empty_cache()
-    ceiling = hbm_read_ceiling(dev)
-    result["extra"]["hbm_read_ceiling_gb_per_s"] = ceiling
-    result["extra"]["decode_frac_of_read_ceiling"] = achieved / ceiling
-    log(f"HBM read ceiling (4 GiB fp32 sum): {ceiling:.0f} GB/s")
+    # torch's own reduction over 4 GiB: a reference point for what a library kernel reads, not
+    # the hardware's ceiling (a plain streaming read reaches more)
+    torch_read = torch_sum_read(dev)
+    result["extra"]["torch_sum_read_gb_per_s"] = torch_read
+    log(f"torch.sum over 4 GiB fp32: {torch_read:.0f} GB/s")
     if not args.no_prefill:
         log("prefill leg ...")
         result["extra"]["prefill"] = prefill_leg(dev)
