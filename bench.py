@@ -150,6 +150,56 @@ def encode_leg(layer, w, device, tokens: int = 32768, reps: int = 10):
             "sample": f"{reps} launches of K and V for {tokens} tokens x {w.n_kv} heads (fp32 source)"}
 
 
+def decode_config_leg(name: str, device, reps: int = 20) -> dict:
+    """One layer of a decode workload timed cold: a read of 768 MiB evicts the 256 MB Infinity
+    Cache before every call (a read, so no dirty lines are written back during the call).
+    Reports the median call time, position-layers/s and GB/s of algorithmic bytes."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    import synth
+    w = synth.WORKLOADS[name]
+    table = synth.placement(w, 0)
+    slots = synth.used_slots(w, table)
+    pool = tq4.Tq4LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+    sd = torch.from_numpy(slots).to(device)
+    for which, st in ((0, synth.T_K), (1, synth.T_V)):
+        src = synth.torch_normal(synth.seed_of(w.wid, 0, st), (len(slots), w.n_kv, 256), device)
+        for c in range(0, len(slots), 65536):
+            part = src[c:c + 65536]
+            tq4.tq4_encode_pages(pool, part if which == 0 else None, part if which == 1 else None,
+                                 sd[c:c + 65536])
+        del src
+    q = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (w.batch, w.n_q, 256), device).to(torch.bfloat16)
+    tab = torch.from_numpy(table).to(device)
+    seq = torch.tensor(w.seq_lens, dtype=torch.int32, device=device)
+    ws = tq4.new_workspace(tq4.tq4_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv,
+                                                              w.page_size), device)
+    out = torch.empty_like(q)
+    call = tq4.prepare_decode(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, out, ws)
+    flush = torch.ones(192 << 20, dtype=torch.float32, device=device)
+    for _ in range(3):
+        call()
+    times = []
+    for _ in range(reps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    t = sorted(times)[reps // 2]
+    positions = sum(w.seq_lens)
+    nbytes = decode_algorithmic_bytes(w.seq_lens, w.page_size, w.n_q)
+    unique = len(slots) * TQ4_BYTES_PER_POS_LAYER
+    del pool, flush
+    torch.cuda.empty_cache()
+    return {"workload": name, "batch": w.batch, "cached_positions": list(w.seq_lens), "page_size": w.page_size,
+            "us_per_call": t * 1e6, "position_layers_per_s": positions / t, "gb_per_s": nbytes / t / 1e9,
+            "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS, "unique_tq4_bytes": unique,
+            "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
+
+
 def prefill_leg(device, reps: int = 3):
     """The chunked-prefill workload: 2,048 bf16 query tokens x 24 heads over 194,560 cached
     positions plus the chunk itself (causal inside the chunk), one layer.  Reports the call
@@ -249,6 +299,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-positions", type=int, default=131072)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the one-layer cold timings of the other decode workloads")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager per-layer launches instead of a HIP graph of the step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -394,6 +446,12 @@ def main() -> int:
     torch_read = torch_sum_read(dev)
     result["extra"]["torch_sum_read_gb_per_s"] = torch_read
     log(f"torch.sum over 4 GiB fp32: {torch_read:.0f} GB/s")
+    if not args.no_configs:
+        result["extra"]["decode_configs"] = []
+        for name in ("decode_1k_p64", "decode_32k", "decode_2req_shared"):
+            r = decode_config_leg(name, dev)
+            result["extra"]["decode_configs"].append(r)
+            log(f"{name}: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s (cold)")
     if not args.no_prefill:
         log("prefill leg ...")
         result["extra"]["prefill"] = prefill_leg(dev)

@@ -38,6 +38,7 @@ constexpr int kPfBlocks = 2;                               // R: 16-row blocks p
 constexpr int kPfRowsPerWg = kPfWaves * kPfBlocks * 16;   // 128
 constexpr int kPfPartial = kDim + 4;                       // O[256], max, sum, pad
 constexpr int kPfTargetWgs = 768;                          // 3 x 256 compute units
+constexpr float kPfRescaleSlack = 8.0f;  // log2 headroom before a running maximum is moved
 
 struct PrefillArgs {
     PrefillParams p;
@@ -226,8 +227,10 @@ void tq4_prefill_kernel(PrefillArgs a) {
             for (int q = 1; q < 8; ++q) mx = fmaxf(mx, sc[q]);
             mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
             mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float m_new = fmaxf(m_run[j], mx);
-            if (__any(m_new > m_run[j])) {
+            // the reference maximum moves only when a score exceeds it by more than the slack
+            // (exp2(s - m_run) <= 256 stays well inside fp16), so rescaling is rare
+            if (__any(mx > m_run[j] + kPfRescaleSlack)) {
+                const float m_new = fmaxf(m_run[j], mx);
                 const float alpha = (m_new > m_run[j]) ? __builtin_amdgcn_exp2f(m_run[j] - m_new) : 1.0f;
                 l_run[j] *= alpha;
 #pragma unroll
