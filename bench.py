@@ -150,10 +150,12 @@ def encode_leg(layer, w, device, tokens: int = 32768, reps: int = 10):
             "sample": f"{reps} launches of K and V for {tokens} tokens x {w.n_kv} heads (fp32 source)"}
 
 
-def decode_config_leg(name: str, device, reps: int = 20) -> dict:
+def decode_config_leg(name: str, device, reps: int = 20, n_queries: int = 1) -> dict:
     """One layer of a decode workload timed cold: a read of 768 MiB evicts the 256 MB Infinity
     Cache before every call (a read, so no dirty lines are written back during the call).
-    Reports the median call time, position-layers/s and GB/s of algorithmic bytes."""
+    Reports the median call time, position-layers/s and GB/s of algorithmic bytes.  With
+    n_queries > 1 the call is the packed verifier: the last n_queries positions of each request
+    attend causally in one pass over its pages."""
     import torch
     import compressed_kv_attention_kvexec_amd as tq4
     import synth
@@ -169,13 +171,19 @@ def decode_config_leg(name: str, device, reps: int = 20) -> dict:
             tq4.tq4_encode_pages(pool, part if which == 0 else None, part if which == 1 else None,
                                  sd[c:c + 65536])
         del src
-    q = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (w.batch, w.n_q, 256), device).to(torch.bfloat16)
+    k = n_queries
+    q = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (w.batch * k, w.n_q, 256), device).to(torch.bfloat16)
     tab = torch.from_numpy(table).to(device)
     seq = torch.tensor(w.seq_lens, dtype=torch.int32, device=device)
-    ws = tq4.new_workspace(tq4.tq4_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv,
+    ws = tq4.new_workspace(tq4.tq4_attn_verify_workspace_size(w.batch, max(w.seq_lens), k, w.n_q, w.n_kv,
                                                               w.page_size), device)
-    out = torch.empty_like(q)
-    call = tq4.prepare_decode(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, out, ws)
+    if k == 1:
+        out = torch.empty_like(q)
+        call = tq4.prepare_decode(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, out, ws)
+    else:
+        q = q.reshape(w.batch, k, w.n_q, 256)
+        out = torch.empty_like(q)
+        call = tq4.prepare_verify(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, out, ws)
     flush = torch.ones(192 << 20, dtype=torch.float32, device=device)
     for _ in range(3):
         call()
@@ -188,16 +196,23 @@ def decode_config_leg(name: str, device, reps: int = 20) -> dict:
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / 1e3)
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError(f"non-finite output ({name}, {k} queries)")
     t = sorted(times)[reps // 2]
     positions = sum(w.seq_lens)
-    nbytes = decode_algorithmic_bytes(w.seq_lens, w.page_size, w.n_q)
+    nbytes = decode_algorithmic_bytes(w.seq_lens, w.page_size, w.n_q) + (k - 1) * w.batch * w.n_q * 256 * 2 * 2
     unique = len(slots) * TQ4_BYTES_PER_POS_LAYER
+    # q.k and p.v products over the keys each query row attends
+    flops = 4 * w.n_q * 256 * sum(max(L - k + i + 1, 0) for L in w.seq_lens for i in range(k))
     del pool, flush
     torch.cuda.empty_cache()
-    return {"workload": name, "batch": w.batch, "cached_positions": list(w.seq_lens), "page_size": w.page_size,
-            "us_per_call": t * 1e6, "position_layers_per_s": positions / t, "gb_per_s": nbytes / t / 1e9,
-            "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS, "unique_tq4_bytes": unique,
-            "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
+    r = {"workload": name, "batch": w.batch, "cached_positions": list(w.seq_lens), "page_size": w.page_size,
+         "us_per_call": t * 1e6, "position_layers_per_s": positions / t, "gb_per_s": nbytes / t / 1e9,
+         "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS, "unique_tq4_bytes": unique,
+         "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
+    if k > 1:
+        r.update({"n_queries": k, "query_tokens_per_s": w.batch * k / t, "tflops": flops / t / 1e12})
+    return r
 
 
 def prefill_leg(device, reps: int = 3):
@@ -301,6 +316,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the one-layer cold timings of the other decode workloads")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip the one-layer cold timings of the packed multi-query verifier")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager per-layer launches instead of a HIP graph of the step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -452,6 +469,13 @@ def main() -> int:
             r = decode_config_leg(name, dev)
             result["extra"]["decode_configs"].append(r)
             log(f"{name}: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s (cold)")
+    if not args.no_verify:
+        result["extra"]["verify"] = []
+        for k in (2, 4, 8):
+            r = decode_config_leg(w.name, dev, n_queries=k)
+            result["extra"]["verify"].append(r)
+            log(f"verify k={k} at {w.seq_lens}: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s, "
+                f"{r['tflops']:.1f} TFLOP/s (cold)")
     if not args.no_prefill:
         log("prefill leg ...")
         result["extra"]["prefill"] = prefill_leg(dev)

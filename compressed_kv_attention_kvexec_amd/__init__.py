@@ -22,7 +22,8 @@ __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_e
            "tq4_attn_decode_workspace_size", "tq4_attn_decode", "tq4_attn_prefill_workspace_size",
            "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library",
            "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill",
-           "tq4_attn_decode_append", "prepare_decode_append"]
+           "tq4_attn_decode_append", "prepare_decode_append", "tq4_attn_verify_workspace_size",
+           "tq4_attn_verify", "prepare_verify"]
 
 HEAD_DIM = 256
 WORDS = 32
@@ -110,6 +111,12 @@ def tq4_attn_decode_workspace_size(batch: int, max_seq_len: int, n_q_heads: int,
                                                               n_kv_heads, page_size))
 
 
+def tq4_attn_verify_workspace_size(batch: int, max_seq_len: int, n_queries: int, n_q_heads: int,
+                                   n_kv_heads: int, page_size: int) -> int:
+    return int(load_library().tq4_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q_heads,
+                                                              n_kv_heads, page_size))
+
+
 def tq4_attn_prefill_workspace_size(prior_len: int, chunk_len: int, n_q_heads: int, n_kv_heads: int,
                                     page_size: int) -> int:
     return int(load_library().tq4_attn_prefill_workspace_size(prior_len, chunk_len, n_q_heads,
@@ -158,6 +165,25 @@ def tq4_attn_decode_append(pool: Tq4LayerPool, k_new, v_new, new_slots: torch.Te
         ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _dtype_code(src), _ptr(new_slots), _ptr(q), _dtype_code(q),
         _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tq4_attn_verify(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                    max_seq_len: int, scale: float, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q [batch][n_queries][n_q][256] bf16: the last n_queries cached positions of each request
+    (seq_lens[b] counts them); query i attends positions 0 .. seq_lens[b] - n_queries + i."""
+    batch, n_queries, n_q, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q, pool.n_kv,
+                                                                 pool.page_size), q.device)
+    ps = pool.struct()
+    check(load_library().tq4_attn_verify(
+        ctypes.byref(ps), _ptr(q), _dtype_code(q), n_queries, _ptr(page_table), int(page_table.shape[1]),
+        _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
@@ -212,6 +238,17 @@ def prepare_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor
             _ptr(seq_lens), batch, int(max_seq_len), n_q, ctypes.c_float(scale), _ptr(out),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     return PreparedCall(load_library().tq4_attn_decode, args, (ps, pool, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_verify(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                   max_seq_len: int, scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                   stream=None) -> PreparedCall:
+    batch, n_queries, n_q, _ = q.shape
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(q), _dtype_code(q), n_queries, _ptr(page_table), int(page_table.shape[1]),
+            _ptr(seq_lens), batch, int(max_seq_len), n_q, ctypes.c_float(scale), _ptr(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return PreparedCall(load_library().tq4_attn_verify, args, (ps, pool, q, page_table, seq_lens, out, workspace))
 
 
 def prepare_prefill(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, prior_len: int,

@@ -63,6 +63,10 @@ def load_library(path: str | None = None):
     lib.tq4_attn_decode_append.argtypes = [pool_p, vp, vp, st, vp, vp, st, vp, i32, vp, i32, i32, i32, f32, vp,
                                            vp, sz, vp]
     lib.tq4_attn_decode_append.restype = st
+    lib.tq4_attn_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.tq4_attn_verify_workspace_size.restype = sz
+    lib.tq4_attn_verify.argtypes = [pool_p, vp, st, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
+    lib.tq4_attn_verify.restype = st
     lib.tq4_attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.tq4_attn_prefill_workspace_size.restype = sz
     lib.tq4_attn_prefill_chunk.argtypes = [pool_p, vp, st, vp, i32, i32, i32, f32, vp, vp, sz, vp]

@@ -103,14 +103,23 @@ size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_
     if (batch < 1 || max_seq_len < 1 || n_kv_heads < 1) return 0;
     if (page_size < 32 || page_size > 1024 || page_size % 32 != 0) return 0;
     if (check_heads(n_q_heads, n_kv_heads) != TQ4_OK) return 0;
-    return tq4::plan_decode(batch, max_seq_len, n_q_heads, n_kv_heads).workspace_bytes;
+    return tq4::plan_decode(batch, max_seq_len, n_q_heads, n_kv_heads, 1).workspace_bytes;
+}
+
+size_t tq4_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_queries, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int32_t page_size) {
+    if (batch < 1 || max_seq_len < 1 || n_kv_heads < 1 || n_queries < 1) return 0;
+    if (page_size < 32 || page_size > 1024 || page_size % 32 != 0) return 0;
+    if (check_heads(n_q_heads, n_kv_heads) != TQ4_OK) return 0;
+    if (int64_t{n_queries} * (n_q_heads / n_kv_heads) > TQ4_MAX_VERIFY_ROWS) return 0;
+    return tq4::plan_decode(batch, max_seq_len, n_q_heads, n_kv_heads, n_queries).workspace_bytes;
 }
 
 namespace {
 
 tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const void *v_new, tq4_dtype src_dtype,
                          const int32_t *new_slots, bool append, const void *q, tq4_dtype q_dtype,
-                         const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
+                         int32_t n_queries, const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
                          int32_t batch, int32_t max_seq_len, int32_t n_q_heads, float scale, void *out,
                          void *workspace, size_t workspace_bytes, void *stream) {
     tq4_status st = check_pool(pool);
@@ -121,6 +130,8 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
     if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
     if (batch < 1 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
     if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
+    if (n_queries < 1 || int64_t{n_queries} * (n_q_heads / pool->n_kv_heads) > TQ4_MAX_VERIFY_ROWS)
+        return TQ4_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return TQ4_ERR_ALIGN;
     if (append) {
@@ -129,7 +140,7 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
         if ((k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)) || !aligned(new_slots, 4))
             return TQ4_ERR_ALIGN;
     }
-    const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads);
+    const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads, n_queries);
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return TQ4_ERR_WORKSPACE;
     if (workspace != nullptr && !aligned(workspace, 256)) return TQ4_ERR_ALIGN;
@@ -167,7 +178,17 @@ tq4_status tq4_attn_decode(const tq4_layer_pool *pool, const void *q, tq4_dtype 
                            const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                            int32_t n_q_heads, float scale, void *out, void *workspace,
                            size_t workspace_bytes, void *stream) {
-    return decode_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, page_table,
+    return decode_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, 1, page_table,
+                         page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace,
+                         workspace_bytes, stream);
+}
+
+tq4_status tq4_attn_verify(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,
+                           const int32_t *page_table, int32_t page_table_stride,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                           int32_t n_q_heads, float scale, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    return decode_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, n_queries, page_table,
                          page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace,
                          workspace_bytes, stream);
 }
@@ -178,7 +199,7 @@ tq4_status tq4_attn_decode_append(const tq4_layer_pool *pool, const void *k_new,
                                   const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                                   int32_t n_q_heads, float scale, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream) {
-    return decode_common(pool, k_new, v_new, src_dtype, new_slots, true, q, q_dtype, page_table,
+    return decode_common(pool, k_new, v_new, src_dtype, new_slots, true, q, q_dtype, 1, page_table,
                          page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace,
                          workspace_bytes, stream);
 }

@@ -34,6 +34,10 @@ hipError_t launch_encode(const EncodeParams &p, hipStream_t stream);
 // workspace query needs no device.
 struct DecodePlan {
     int32_t group;        // n_q_heads / n_kv_heads
+    int32_t n_queries;    // query tokens per request (1: decode)
+    int32_t rows;         // n_queries * group query rows per (request, KV head)
+    int32_t col_blocks;   // 16-column MFMA blocks holding the rows
+    int32_t waves;        // wavefronts per split workgroup
     int32_t n_splits;     // workgroups per (request, KV head)
     int32_t split_tiles;  // 32-key tiles per workgroup
     size_t counters_bytes;
@@ -41,7 +45,8 @@ struct DecodePlan {
     size_t workspace_bytes;
 };
 
-DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads);
+DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t n_queries);
 
 struct DecodeParams {
     const uint32_t *k_words;
@@ -51,7 +56,7 @@ struct DecodeParams {
     int32_t num_pages;
     int32_t page_size;
     int32_t n_kv;
-    const uint16_t *q;  // bf16 bits [batch][n_q][256]
+    const uint16_t *q;  // bf16 bits [batch][n_queries][n_q][256]
     const int32_t *page_table;
     int32_t table_stride;
     const int32_t *seq_lens;
@@ -59,7 +64,7 @@ struct DecodeParams {
     int32_t max_seq_len;
     int32_t n_q;
     float scale;
-    uint16_t *out;  // bf16 bits [batch][n_q][256]
+    uint16_t *out;  // bf16 bits [batch][n_queries][n_q][256]
     void *workspace;
     // optional: encode one new token per request before attending (NULL k_new and v_new: none)
     const void *k_new;  // [batch][n_kv][256] fp32 or bf16

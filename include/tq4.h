@@ -78,6 +78,7 @@ extern "C" {
 #define TQ4_WORDS_PER_VECTOR 32
 #define TQ4_NUM_CENTROIDS 16
 #define TQ4_MAX_GROUP 16 /* largest n_q_heads / n_kv_heads */
+#define TQ4_MAX_VERIFY_ROWS 48 /* largest n_queries * n_q_heads / n_kv_heads of tq4_attn_verify */
 
 typedef enum tq4_status {
     TQ4_OK = 0,
@@ -197,6 +198,44 @@ tq4_status tq4_attn_decode_append(const tq4_layer_pool *pool, const void *k_new,
                                   const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                                   int32_t n_q_heads, float scale, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace tq4_attn_verify needs for these sizes (0 for
+ * invalid sizes, and 0 when one workgroup covers each request and KV head).
+ * With n_queries == 1 it equals tq4_attn_decode_workspace_size.
+ */
+size_t tq4_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_queries,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t page_size);
+
+/*
+ * tq4_attn_verify -- packed multi-query attention on the packed pages: the
+ * last n_queries positions of each request (speculative draft tokens being
+ * verified, or a short chunk) attend causally in one pass over the request's
+ * pages ([KVX]: besides direct reconstruction, multi-query prefill has a
+ * packed verifier path).  All n_queries x group query rows of one KV head
+ * share every page read, so the pages are streamed once, not n_queries times.
+ *
+ *   q         : device [batch][n_queries][n_q_heads][256], q_dtype ==
+ *               TQ4_BF16, 16-byte aligned.
+ *   n_queries : >= 1 with n_queries * (n_q_heads / n_kv_heads) <=
+ *               TQ4_MAX_VERIFY_ROWS.
+ *   seq_lens  : device int32 [batch]; cached positions of each request
+ *               including its n_queries query tokens, whose K/V are already
+ *               encoded.  Clamped to [0, max_seq_len] as L; query token i sits
+ *               at position L - n_queries + i and attends positions
+ *               0 .. L - n_queries + i; a query with no such position (L <
+ *               n_queries - i) gets a zero output.
+ *   out       : device [batch][n_queries][n_q_heads][256] in q_dtype.
+ *   workspace : device, >= tq4_attn_verify_workspace_size(...) bytes, as for
+ *               tq4_attn_decode.
+ *   other arguments as for tq4_attn_decode.  With n_queries == 1 the result
+ *   is bit-identical to tq4_attn_decode.
+ */
+tq4_status tq4_attn_verify(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,
+                           const int32_t *page_table, int32_t page_table_stride,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                           int32_t n_q_heads, float scale, void *out, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace tq4_attn_prefill_chunk needs (0 for invalid sizes). */
 size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,

@@ -278,6 +278,21 @@ def attn_decode(pool: Pool, q, page_table, seq_lens, scale: float, heads=None) -
                      np.asarray(seq_lens, np.int32), scale, heads)
 
 
+def attn_verify(pool: Pool, q, page_table, seq_lens, scale: float, heads=None) -> np.ndarray:
+    """Packed multi-query verification ("Fitting a 27B-Parameter LLM into 24 GiB of Laptop Memory",
+    section "KVExec: Fused Reconstruction with Layer-Scoped Lifetime": a packed verifier is one of
+    the multi-query paths).  q: [batch][k][n_q][256]; the k queries of request b are its last k
+    cached positions, so query i sits at position L - k + i (L = seq_lens[b]) and attends positions
+    0 .. L - k + i; a query with no such position gets zeros.  Returns [batch][k][n_q][256]."""
+    q = np.asarray(q)
+    batch, k = q.shape[0], q.shape[1]
+    L = np.asarray(seq_lens, np.int64)
+    rows = np.repeat(np.arange(batch, dtype=np.int32), k)
+    lens = np.maximum(L[:, None] - k + np.arange(k)[None, :] + 1, 0).reshape(-1).astype(np.int32)
+    out = attention(pool, q.reshape(batch * k, q.shape[2], DIM), page_table, rows, lens, scale, heads)
+    return out.reshape(q.shape)
+
+
 def attn_prefill_rows(pool: Pool, q_rows, rows, page_table_row, prior_len: int, scale: float,
                       heads=None) -> np.ndarray:
     """Chunk rows t (absolute position prior_len + t) attend positions 0..prior_len + t."""

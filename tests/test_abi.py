@@ -86,6 +86,33 @@ def test_decode_workspace_size_is_bounded(lib):
     assert ws(2, 131072, 24, 4, 256) >= ws(1, 131072, 24, 4, 256)
 
 
+def _verify(lib, n_queries=4, n_q=24, ws=FAKE, ws_bytes=1 << 30, pool=None, q=FAKE):
+    pool = _pool() if pool is None else pool
+    return lib.tq4_attn_verify(ctypes.byref(pool), q, B.TQ4_BF16, n_queries, FAKE, 64, FAKE, 1, 4000, n_q,
+                               0.0625, FAKE, ws, ws_bytes, None)
+
+
+def test_verify_validation(lib):
+    assert _verify(lib, n_queries=0) == 2
+    assert _verify(lib, n_queries=9) == 2        # 9 x 6 = 54 query rows > 48
+    assert _verify(lib, n_queries=4, n_q=64) == 2  # 4 x 16 = 64 rows
+    assert _verify(lib, n_q=22) == 2
+    assert _verify(lib, q=None) == 1
+    assert _verify(lib, q=FAKE + 2) == 4
+    assert _verify(lib, ws=None) == 5
+    vs = lib.tq4_attn_verify_workspace_size
+    assert vs(1, 4000, 0, 24, 4, 64) == 0
+    assert vs(1, 4000, 9, 24, 4, 64) == 0
+    assert vs(1, 4000, 8, 24, 4, 64) > 0         # 48 rows: the largest packing
+    # one query is decode
+    for args in [(1, 4000, 24, 4, 64), (3, 212992, 24, 4, 256), (1, 200, 24, 4, 64), (2, 5000, 64, 4, 32)]:
+        b, L, nq, nkv, P = args
+        assert vs(b, L, 1, nq, nkv, P) == lib.tq4_attn_decode_workspace_size(*args)
+    need = vs(1, 4000, 4, 24, 4, 64)
+    assert need > lib.tq4_attn_decode_workspace_size(1, 4000, 24, 4, 64)
+    assert _verify(lib, ws_bytes=need - 1) == 5
+
+
 def test_encode_validation(lib):
     pool = _pool()
     enc = lib.tq4_encode_pages

@@ -77,37 +77,71 @@ def _mpf(fr):
     return mpmath.mpf(fr.numerator) / fr.denominator
 
 
-def test_brute_force_50_digits(oracle_mod):
-    """Dense Hadamard decode in exact rationals and softmax in 50-digit arithmetic."""
-    mpmath.mp.dps = 50
+def _exact_records(oracle_mod, pool, table, L, g):
+    """Decoded K and V of positions 0..L-1 of KV head g in exact rationals (dense Hadamard)."""
     c, _ = oracle_mod.codebook()
     cF = [Fraction(float(v)) for v in c]
     H = scipy.linalg.hadamard(256)
+    dec = {}
+    for which in ("k", "v"):
+        w, n = _records(pool, table, L, g, which)
+        idx = oracle_mod.unpack(w)
+        vecs = []
+        for j in range(L):
+            nj = Fraction(float(np.uint16(n[j]).view(np.float16)))
+            ys = np.array([cF[i] for i in idx[j]], dtype=object)
+            vecs.append([nj * sum(int(H[d, t]) * ys[t] for t in range(256)) / 16 for d in range(256)])
+        dec[which] = vecs
+    return dec
+
+
+def _mp_attention(q_row, dec, n_keys, dims):
+    """50-digit softmax attention of one query row over the first n_keys decoded positions."""
+    qh = [Fraction(float(v)) for v in q_row]
+    s = [_mpf(sum(a * b for a, b in zip(qh, dec["k"][j]))) / 16 for j in range(n_keys)]
+    mx = max(s)
+    e = [mpmath.exp(x - mx) for x in s]
+    tot = sum(e)
+    return [sum(e[j] * _mpf(dec["v"][j][d]) for j in range(n_keys)) / tot for d in dims]
+
+
+def test_brute_force_50_digits(oracle_mod):
+    """Dense Hadamard decode in exact rationals and softmax in 50-digit arithmetic."""
+    mpmath.mp.dps = 50
+    dims = (0, 5, 128, 255)
     for L, seed in [(1, 21), (3, 22), (8, 23)]:
         pool, table = _rand_pool(oracle_mod, 3, 2, 64, L, seed)
         q = _bf16_q(1, 4, seed + 100, scale=4.0)      # peaked softmax
         out = oracle_mod.attn_decode(pool, q, table[None], [L], 1 / 16)
         for g in range(2):
-            dec = {}
-            for which in ("k", "v"):
-                w, n = _records(pool, table, L, g, which)
-                idx = oracle_mod.unpack(w)
-                vecs = []
-                for j in range(L):
-                    nj = Fraction(float(np.uint16(n[j]).view(np.float16)))
-                    ys = np.array([cF[i] for i in idx[j]], dtype=object)
-                    vecs.append([nj * sum(int(H[d, t]) * ys[t] for t in range(256)) / 16
-                                 for d in range(256)])
-                dec[which] = vecs
+            dec = _exact_records(oracle_mod, pool, table, L, g)
             for h in (2 * g, 2 * g + 1):
-                qh = [Fraction(float(v)) for v in q[0, h]]
-                s = [_mpf(sum(a * b for a, b in zip(qh, dec["k"][j]))) / 16 for j in range(L)]
-                mx = max(s)
-                e = [mpmath.exp(x - mx) for x in s]
-                tot = sum(e)
-                for d in (0, 5, 128, 255):
-                    ref = sum(e[j] * _mpf(dec["v"][j][d]) for j in range(L)) / tot
-                    assert abs(float(ref) - out[0, h, d]) <= 1e-12 * max(1.0, abs(float(ref)))
+                ref = _mp_attention(q[0, h], dec, L, dims)
+                for d, r in zip(dims, ref):
+                    assert abs(float(r) - out[0, h, d]) <= 1e-12 * max(1.0, abs(float(r)))
+
+
+def test_verify_brute_force_50_digits(oracle_mod):
+    """Packed verification of k = 3 queries over L = 5 positions: query i sees L - k + i + 1 keys
+    (3, 4, 5), checked against the 50-digit brute force; with L = 2 < k the first query sees
+    nothing (zeros) and the second sees one key (its value vector)."""
+    mpmath.mp.dps = 50
+    dims = (1, 64, 200)
+    L, k = 5, 3
+    pool, table = _rand_pool(oracle_mod, 3, 1, 64, L, 61)
+    q = _bf16_q(k, 2, 62, scale=4.0).reshape(1, k, 2, 256)
+    out = oracle_mod.attn_verify(pool, q, table[None], [L], 1 / 16)
+    dec = _exact_records(oracle_mod, pool, table, L, 0)
+    for i in range(k):
+        for h in range(2):
+            ref = _mp_attention(q[0, i, h], dec, L - k + i + 1, dims)
+            for d, r in zip(dims, ref):
+                assert abs(float(r) - out[0, i, h, d]) <= 1e-12 * max(1.0, abs(float(r)))
+    short = oracle_mod.attn_verify(pool, q, table[None], [2], 1 / 16)
+    assert np.all(short[0, 0] == 0.0)
+    for h in range(2):
+        for d in dims:
+            assert abs(float(_mpf(dec["v"][0][d])) - short[0, 1, h, d]) <= 1e-12
 
 
 def test_gqa_heads_read_their_group(oracle_mod):
@@ -150,3 +184,23 @@ def test_prefill_rows_are_causal(oracle_mod):
         np.testing.assert_array_equal(out[r], ref[0])
         shorter = oracle_mod.attn_decode(pool, q[t:t + 1], table[None], [prior + t], 1 / 16)
         assert np.any(out[r] != shorter[0])
+
+
+def test_verify_rows_are_causal(oracle_mod):
+    """Query i of k over L cached positions equals decode at length L - k + i + 1 and differs from
+    decode one position shorter; k = 1 is decode."""
+    k = 4
+    pool, table = _rand_pool(oracle_mod, 6, 2, 64, 300, 71)
+    tables = np.stack([table, table])
+    lens = [300, 130]
+    q = _bf16_q(2 * k, 4, 72).reshape(2, k, 4, 256)
+    out = oracle_mod.attn_verify(pool, q, tables, lens, 1 / 16)
+    for b in range(2):
+        for i in range(k):
+            n = lens[b] - k + i + 1
+            ref = oracle_mod.attn_decode(pool, q[b, i][None], table[None], [n], 1 / 16)
+            np.testing.assert_array_equal(out[b, i], ref[0])
+            shorter = oracle_mod.attn_decode(pool, q[b, i][None], table[None], [n - 1], 1 / 16)
+            assert np.any(out[b, i] != shorter[0])
+    one = oracle_mod.attn_verify(pool, q[:, :1], tables, lens, 1 / 16)
+    np.testing.assert_array_equal(one[:, 0], oracle_mod.attn_decode(pool, q[:, 0], tables, lens, 1 / 16))
