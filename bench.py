@@ -27,7 +27,7 @@ TQ4_BYTES_PER_POS_LAYER = 4 * 2 * 130  # 4 KV heads x (K, V) x (128 B words + 2 
 EVENT_EVERY = 4  # time every 4th layer's call with events (fewer markers in the timed stream)
 
 
-DECODE_PROFILE = os.path.join(ROOT, "profiles", "tq4_decode_kernel_decode_212k_16l.md")
+DECODE_PROFILE = os.path.join(ROOT, "profiles", "tq4_attn_split_kernel_decode_212k_16l.md")
 DECODE_SOURCES = ["compressed_kv_attention_kvexec_amd/csrc/tq4_decode.hip",
                   "compressed_kv_attention_kvexec_amd/csrc/tq4_tile.h",
                   "compressed_kv_attention_kvexec_amd/csrc/tq4_device.h"]
@@ -444,7 +444,7 @@ def main() -> int:
                    "query_dtype": "bf16"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "tq4_attn_decode_append call = tq4_decode_kernel + tq4_decode_combine_kernel",
+                     "kernel": "tq4_attn_decode_append call = tq4_attn_split_kernel<1, 8> + tq4_decode_combine_kernel",
                      "bytes_per_launch": bytes_launch, "avg_launch_us": avg_dec_s * 1e6},
         "extra": {"step_hbm_gb_per_s": step_gbs, "step_frac_of_peak": step_gbs / HBM_PEAK_GBS,
                   "execution": "hip graph of the step's 16 calls" if elapsed_graph is not None else "eager launches",

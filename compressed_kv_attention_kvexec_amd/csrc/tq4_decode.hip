@@ -1,4 +1,5 @@
-// tq4_decode.hip -- single-query decode attention directly on TQ4 pages, gfx950.
+// tq4_decode.hip -- decode attention directly on TQ4 pages, gfx950: one query token per request
+// (decode) or its last n_queries tokens at once (the packed multi-query verifier).
 //
 // What is computed ("Fitting a 27B-Parameter LLM into 24 GiB of Laptop
 // Memory", section "KVExec: Fused Reconstruction with Layer-Scoped Lifetime";
@@ -12,17 +13,18 @@
 // so a page is consumed as 4-bit indices -> centroid values -> products,
 // with no per-key Hadamard and no float K/V outside registers and LDS.
 //
-// Work decomposition: grid (split, KV head, request); 8 wavefronts per
-// workgroup; a wavefront owns every 8th 32-key tile of its workgroup's range.
-// Per tile and wavefront (GQA group of G <= 16 query heads padded to 16):
-//   S^T[32 keys][16 heads] = K_tile . Q_rot^T   16 x v_mfma_f32_16x16x32_f16
-//   online softmax in base 2 (key norms in the scores, value norms in P)
-//   O^T[256][16 heads] += V_tile^T . P^T        16 x v_mfma_f32_16x16x32_f16
+// Work decomposition: grid (split, KV head, request).  The query rows of a KV head (G heads x
+// n_queries tokens) are MFMA columns, 16 per block; a wavefront owns one block and every NS-th
+// 32-key tile of its workgroup's range (decode: one block, 8 wavefronts).  Per tile and
+// wavefront:
+//   S^T[32 keys][16 rows] = K_tile . Q_rot^T   16 x v_mfma_f32_16x16x32_f16
+//   online softmax in base 2 (key norms in the scores, value norms in P, a causal limit per row)
+//   O^T[256][16 rows] += V_tile^T . P^T        16 x v_mfma_f32_16x16x32_f16
 // Operand layouts and the centroid table are described in tq4_tile.h.  The
 // workgroup merges its wavefronts in LDS; with several splits it leaves
 // (max, sum, accumulator) in the workspace and tq4_decode_combine_kernel merges
 // the splits in fixed order, applies the inverse rotation and writes bf16.
-#include <type_traits>
+#include <cfloat>
 
 #include "tq4_device.h"
 #include "tq4_encode_wave.h"
@@ -39,7 +41,8 @@ constexpr int kPlanWgsPerCU = 1;    // resident decode workgroups per CU
 constexpr int kMinTilesPerWave = 2;
 constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running maximum is moved
 
-constexpr int kDecStatPad = 64;  // floats of each statistic row in a split partial (rows <= 64)
+constexpr int kDecStatPad = 64;
+  // floats of each statistic row in a split partial (rows <= 64)
 
 struct DecodeArgs {
     DecodeParams p;
@@ -62,11 +65,11 @@ DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, in
     pl.n_queries = n_queries;
     pl.rows = n_queries * pl.group;
     pl.col_blocks = (pl.rows + 15) / 16;
-    pl.waves = pl.col_blocks == 1 ? kDecWaves : kDecWaves / 2;
+    pl.slots = pl.col_blocks == 1 ? kDecWaves : kDecWaves / 2;  // tile slots per workgroup
     const int64_t tiles = (static_cast<int64_t>(max_seq_len) + kTile - 1) / kTile;
     const int64_t units = static_cast<int64_t>(batch) * n_kv_heads;
     int64_t want = (static_cast<int64_t>(kPlanCUs) * kPlanWgsPerCU + units - 1) / units;
-    const int64_t cap = (tiles + pl.waves * kMinTilesPerWave - 1) / (pl.waves * kMinTilesPerWave);
+    const int64_t cap = (tiles + pl.slots * kMinTilesPerWave - 1) / (pl.slots * kMinTilesPerWave);
     if (want > cap) want = cap;
     if (want > kMaxSplits) want = kMaxSplits;
     if (want < 1) want = 1;
@@ -83,18 +86,21 @@ DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, in
 
 // ---------------------------------------------------------------- split kernel
 
-// NC blocks of 16 MFMA columns hold the query rows of one (request, KV head): row r = i G + h for
-// query token i (of n_queries) and head h of the group.  NW wavefronts per workgroup.  Decode is
-// NC = 1, NW = 8 (two wavefronts per SIMD); the multi-query verifier with more than 16 rows uses
-// NC = 2 or 3 with NW = 4 (one wavefront per SIMD, for the 64 accumulators of each extra block).
-template <int NC, int NW>
-__global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a) {
+// The query rows of one (request, KV head) -- row r = i G + h for query token i of n_queries and
+// head h of the group -- fill NB blocks of 16 MFMA columns.  A workgroup has NS tile slots per
+// block: wavefront w = blk NS + slot owns column block blk and every NS-th tile from its slot, so
+// the NB wavefronts of a slot read the same tiles (one HBM read, the others hit the caches) and
+// each keeps one block's 64 accumulators.  Decode is NB = 1, NS = 8 (two wavefronts per SIMD);
+// the multi-query verifier uses NB = 2 or 3 with NS = 4 (two or three per SIMD).
+template <int NB, int NS>
+__global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeArgs a) {
+    constexpr int NW = NB * NS;
     constexpr int NT = NW * kWave;
-    constexpr int NCOL = 16 * NC;
+    constexpr int NCOL = 16 * NB;
     __shared__ __align__(16) uint32_t lut_mem[kLutWords];
-    __shared__ __align__(16) half8 qop_sh[NC][8][kWave];  // rotated-query operand per block, K-step, lane
-    __shared__ float stat_m[NW][NCOL];
-    __shared__ float stat_l[NW][NCOL];
+    __shared__ __align__(16) half8 qop_sh[NB][8][kWave];  // rotated-query operand per block, K-step, lane
+    __shared__ float stat_m[NW][16];
+    __shared__ float stat_l[NW][16];
     __shared__ float row_f[NCOL];
     __shared__ float resM[NCOL];
     __shared__ float resL[NCOL];
@@ -110,6 +116,7 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
 
     const int L_req = p.seq_lens[b];  // scalar load, requested first; used after the tile issue
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int slot = wave_u % NS, blk = wave_u / NS;
     const int split_keys = a.split_tiles * kTile;
     const int key_begin = s * split_keys;
     const int32_t *pt_row = p.page_table + static_cast<int64_t>(b) * p.table_stride;
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
     // request's length and can fly alongside it; entries past the length are never used.
     int pid_vec = 0;
     auto fetch_pids = [&](int chunk) {
-        const int tile = wave_u + (chunk * kWave + lane) * NW;
+        const int tile = slot + (chunk * kWave + lane) * NS;
         pid_vec = pt_row[min((key_begin + tile * kTile) / p.page_size, p.table_stride - 1)];
     };
     auto pid_of = [&](int j) -> int { return __builtin_amdgcn_readlane(pid_vec, j & (kWave - 1)); };
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
     // compiler's wait counts stay exact through the prologue.
     const u32x2 q_raw0 = *reinterpret_cast<const u32x2 *>(p.q + row_off(min(wave_u, ROWS - 1)) + 4 * lane);
     fetch_pids(0);
-    issue(wave_u, 0, true);
+    issue(slot, 0, true);
 
     const int L = L_req < 0 ? 0 : (L_req > p.max_seq_len ? p.max_seq_len : L_req);
     const int n_active = (L + split_keys - 1) / split_keys;
@@ -173,11 +180,12 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
     }
     const int key_end = min(key_begin + split_keys, L);
     const int n_tiles = (key_end - key_begin + kTile - 1) / kTile;
-    const int n_mine = wave_u < n_tiles ? (n_tiles - wave_u + NW - 1) / NW : 0;
+    const int n_mine = slot < n_tiles ? (n_tiles - slot + NS - 1) / NS : 0;
 
     // ---- prologue: fill the centroid table and the rotated-query operand (each column written
     // once: query rows by the wavefront r % NW, padding columns zeroed), one barrier
-    build_lut<NT>(lut_mem, a.lut_pairs, tid);
+    constexpr int kLutThreads = NT >= 1024 ? 1024 : (NT >= 512 ? 512 : 256);  // the first waves fill it
+    if (tid < kLutThreads) build_lut<kLutThreads>(lut_mem, a.lut_pairs, tid);
     if (tid < NW) progress[tid] = 0;
     auto rotate_row = [&](int r, u32x2 raw) {
         // one wavefront rotates query row r: y = H q (unnormalised), then a power-of-two scale
@@ -220,12 +228,13 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
     // loads it, so that wavefront writes the new token's K and V records (position seq_len - 1)
     // here, before its loop; if its first tile, requested above, is that last tile, it requests it
     // again.
-    if constexpr (NC == 1) {
-        if (append_mode && s == n_active - 1 && n_tiles > 0 && wave_u == (n_tiles - 1) % NW) {
-            const int slot = p.new_slots[b];
-            if (slot >= 0 && slot < p.num_pages * p.page_size) {
-                const int page = slot / p.page_size;
-                const int64_t rec = (static_cast<int64_t>(page) * p.n_kv + g) * p.page_size + (slot - page * p.page_size);
+    if constexpr (NB == 1) {
+        if (append_mode && s == n_active - 1 && n_tiles > 0 && slot == (n_tiles - 1) % NS) {
+            const int slot_new = p.new_slots[b];
+            if (slot_new >= 0 && slot_new < p.num_pages * p.page_size) {
+                const int page = slot_new / p.page_size;
+                const int64_t rec =
+                    (static_cast<int64_t>(page) * p.n_kv + g) * p.page_size + (slot_new - page * p.page_size);
                 const size_t off = (static_cast<size_t>(b) * p.n_kv + g) * kDim * (p.new_bf16 ? 2 : 4);
                 float xk[4], xv[4];
                 if (p.k_new != nullptr) encode_load(static_cast<const char *>(p.k_new) + off, p.new_bf16 != 0, lane, xk);
@@ -241,37 +250,28 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
             // wavefront loads the last tile (vmcnt bits [3:0] and [15:14] zero, expcnt and
             // lgkmcnt left at max)
             __builtin_amdgcn_s_waitcnt(0x0F70);
-            if (n_mine == 1) issue(wave_u, 0, true);
+            if (n_mine == 1) issue(slot, 0, true);
         }
     }
-    // per lane and block: score factor of column n and its causal limit (visible keys: query
-    // token i sees positions 0 .. L - KQ + i; padding columns see everything and weigh nothing)
-    float fcol[NC];
-    int lim_col[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int r = 16 * c + n;
-        fcol[c] = r < ROWS ? row_f[r] : 0.f;
-        lim_col[c] = r < ROWS ? L - KQ + r / G + 1 : L;
-    }
+    // this lane's column r = 16 blk + n: score factor and causal limit (visible keys: query token
+    // i sees positions 0 .. L - KQ + i; padding columns see everything and are never written)
+    const int col = 16 * blk + n;
+    const float fcol = col < ROWS ? row_f[col] : 1.f;
+    const int lim_col = col < ROWS ? L - KQ + col / G + 1 : L;
+    const half8 *qop = &qop_sh[blk][0][lane];
     const char *lut = reinterpret_cast<const char *>(lut_mem);
     const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;
 
-    float4v oacc[NC][16];
-    float m_run[NC], l_run[NC];
+    float4v oacc[16];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) oacc[c][t] = float4v{0.f, 0.f, 0.f, 0.f};
-        m_run[c] = -INFINITY;
-        l_run[c] = 0.f;
-    }
+    for (int t = 0; t < 16; ++t) oacc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
 
-    // One tile per step, its register set refilled in place with tile t + NW: the next K is
+    // One tile per step, its register set refilled in place with tile t + NS: the next K is
     // requested as soon as this tile's scores exist, the next V as soon as its P.V products are
     // issued.  live == false makes the refill a dead load (past the chunk's end).
-    // Issue priority (two wavefronts per SIMD): the pair w, w ^ 4 would otherwise be served oldest
-    // first, and the younger one would finish its equal share of tiles much later.  Each
+    // Issue priority (two wavefronts per SIMD, w and w ^ 4): the pair has equal shares of tiles
+    // but would be served oldest first, so the younger one would finish much later.  Each
     // wavefront publishes how many tiles it has started; the younger one takes the higher
     // priority while it is not ahead of its partner, the older one only while it is behind.
     // Tile assignment stays static, so results do not depend on timing.
@@ -286,20 +286,17 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
         }
         const int key0 = key_begin + t * kTile;
         const bool valid = valid_t;
-        // ---- scores S^T (rows: keys, columns: query rows), one decode of K for every block
-        float4v sacc[NC][2];
+        // ---- scores S^T (rows: keys, columns: query rows)
+        float4v sacc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) sacc[c][mt] = float4v{0.f, 0.f, 0.f, 0.f};
+            sacc[mt] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 const u32x4 kw = kr.k[mt][ks >> 2];
                 const uint32_t w = (ks & 3) == 0 ? kw.x : (ks & 3) == 1 ? kw.y : (ks & 3) == 2 ? kw.z : kw.w;
                 const half8 kop = lut_decode(w, lane4, lut);
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    sacc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop_sh[c][ks][lane], sacc[c][mt], 0, 0, 0);
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[ks * kWave], sacc[mt], 0, 0, 0);
             }
         }
         // lane holds column n, keys sigma(j): j < 4 -> 4gq + j, else 16 + 4gq + j - 4
@@ -311,19 +308,17 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
             kn[4 * h + 2] = f16lo(kr.kn[h].y);
             kn[4 * h + 3] = f16hi(kr.kn[h].y);
         }
-        float sc[NC][8];
+        // x = (q_rot . c[idx]) n_k; the score in log2 units is fcol x.  Masked keys get -inf.
+        float xs[8];
+        const int lim = valid ? (min(key_end, lim_col) - key0) : 0;  // keys at offset >= lim are masked
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int lim = valid ? (min(key_end, lim_col[c]) - key0) : 0;  // keys at offset >= lim are masked
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int koff = 16 * h + 4 * gq + r;
-                    sc[c][4 * h + r] = (koff < lim) ? sacc[c][h][r] * kn[4 * h + r] * fcol[c] : -INFINITY;
-                }
-        }
-        const int64_t rec = rec_of(t + NW, inext, valid_t);
+            for (int r = 0; r < 4; ++r) {
+                const int koff = 16 * h + 4 * gq + r;
+                xs[4 * h + r] = (koff < lim) ? sacc[h][r] * kn[4 * h + r] : -INFINITY;
+            }
+        const int64_t rec = rec_of(t + NS, inext, valid_t);
         const int64_t rec_pf = live ? rec : 0;
         const LaneOffsets ofs_pf = live ? lofs : dead_ofs;
         __builtin_amdgcn_sched_barrier(0);
@@ -343,44 +338,43 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
             nv[4 * h + 2] = f16lo(vr.vn[h].y);
             nv[4 * h + 3] = f16hi(vr.vn[h].y);
         }
-        half8 pop[NC];
+        float mx = xs[0];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float mx = sc[c][0];
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, xs[j]);
+        float lo, hi;  // column n's maximum over the four lane groups
+        lane_pair<16>(mx, lo, hi);
+        mx = fmaxf(lo, hi);
+        lane_pair<32>(mx, lo, hi);
+        mx = fmaxf(lo, hi) * fcol;  // fcol > 0
+        // The reference maximum moves only when a score exceeds it by more than kRescaleSlack (so
+        // exp2(s - m_run) <= 256, well inside fp16): the softmax does not depend on the reference,
+        // and rescaling the 64 accumulators becomes rare.  This lane's accumulators all belong to
+        // column n, so the rescale factor is lane-local.
+        if (__any(mx > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
 #pragma unroll
-            for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[c][j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            // The reference maximum moves only when a score exceeds it by more than kRescaleSlack
-            // (so exp2(s - m_run) <= 256, well inside fp16): the softmax does not depend on the
-            // reference, and rescaling the 64 accumulators becomes rare.  This lane's
-            // accumulators all belong to column n, so the rescale factor is lane-local.
-            if (__any(mx > m_run[c] + kRescaleSlack)) {
-                const float m_new = fmaxf(m_run[c], mx);
-                const float alpha = (m_new > m_run[c]) ? __builtin_amdgcn_exp2f(m_run[c] - m_new) : 1.0f;
-                l_run[c] *= alpha;
-#pragma unroll
-                for (int tt = 0; tt < 16; ++tt) oacc[c][tt] *= alpha;
-                m_run[c] = m_new;
-            }
-            float pv[8];
-            const bool col_live = 16 * c + n < ROWS;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float sj = sc[c][j];
-                const float e = (sj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sj - m_run[c]);
-                l_run[c] += e;
-                pv[j] = col_live ? e * nv[j] : 0.f;
-            }
-            u32x4 pr;
-            pr.x = pack_f16x2(pv[0], pv[1]);
-            pr.y = pack_f16x2(pv[2], pv[3]);
-            pr.z = pack_f16x2(pv[4], pv[5]);
-            pr.w = pack_f16x2(pv[6], pv[7]);
-            pop[c] = __builtin_bit_cast(half8, pr);
+            for (int tt = 0; tt < 16; ++tt) oacc[tt] *= alpha;
+            m_run = m_new;
         }
-        // ---- O^T[dims][columns] += V^T P^T over two word columns (words 2n and 2n+1 of each
-        // key), one decode of V for every block
+        // m_run is -inf only while every key of the column so far was masked; the floor keeps
+        // fcol x - m finite or -inf then, and exp2(-inf) = 0 drops masked keys
+        const float neg_m = -fmaxf(m_run, -FLT_MAX);
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[j], fcol, neg_m));
+            l_run += e;
+            pv[j] = e * nv[j];
+        }
+        u32x4 pr;
+        pr.x = pack_f16x2(pv[0], pv[1]);
+        pr.y = pack_f16x2(pv[2], pv[3]);
+        pr.z = pack_f16x2(pv[4], pv[5]);
+        pr.w = pack_f16x2(pv[6], pv[7]);
+        const half8 pop = __builtin_bit_cast(half8, pr);
+        // ---- O^T[dims][columns] += V^T P^T over two word columns (words 2n and 2n+1 of each key)
 #pragma unroll
         for (int cw = 0; cw < 2; ++cw) {
             uint32_t wv[8], u[8];
@@ -390,9 +384,7 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const half8 vop = lut_decode(u[i], lane4, lut);
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    oacc[c][8 * cw + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[c], oacc[c][8 * cw + i], 0, 0, 0);
+                oacc[8 * cw + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, oacc[8 * cw + i], 0, 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -403,128 +395,115 @@ __global__ __launch_bounds__(NW * kWave) void tq4_attn_split_kernel(DecodeArgs a
     // ---- main loop over chunks of 64 tiles (one VGPR of page IDs)
     for (int c0 = 0; c0 < n_mine; c0 += kWave) {
         const int cn = min(kWave, n_mine - c0);
-        const int tc = wave_u + c0 * NW;  // first tile of the chunk
+        const int tc = slot + c0 * NS;  // first tile of the chunk
         if (c0 > 0) {
             fetch_pids(c0 / kWave);
             issue(tc, 0, true);
         }
-        for (int i = 0; i < cn; ++i) step(tc + i * NW, i + 1, i + 1 < cn, c0 + i);
+        for (int i = 0; i < cn; ++i) step(tc + i * NS, i + 1, i + 1 < cn, c0 + i);
     }
     if constexpr (kPaired) __builtin_amdgcn_s_setprio(0);
 
     // ---- per-wave softmax totals
-    float l_tot[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        l_tot[c] = l_run[c] + __shfl_xor(l_run[c], 16, kWave);
-        l_tot[c] = l_tot[c] + __shfl_xor(l_tot[c], 32, kWave);
-    }
+    float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+    l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
     __syncthreads();  // table no longer needed
     if (gq == 0) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            stat_m[wave][16 * c + n] = m_run[c];
-            stat_l[wave][16 * c + n] = l_tot[c];
-        }
+        stat_m[wave][n] = m_run;
+        stat_l[wave][n] = l_tot;
     }
     __syncthreads();
 
-    // ---- merge the workgroup's waves.  Each lane rescales its accumulators (all of column n) to
-    // the workgroup maximum; then, block by block, a fixed-order tree in LDS adds waves
-    // NW/2 .. NW-1 into 0 .. NW/2-1, and so on down to wave 0.  The LDS image keeps the
-    // accumulator lane layout ([wave][register][lane] as 16-byte rows), so every access is
-    // conflict-free.
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    // ---- merge the waves of each block.  Each lane rescales its accumulators (all of column n)
+    // to the block's maximum over its waves; then a fixed-order tree in LDS adds slots
+    // NS/2 .. NS-1 into 0 .. NS/2-1, and so on down to slot 0.  The LDS image keeps the
+    // accumulator lane layout ([block][slot][register][lane] as 16-byte rows), so every access is
+    // conflict-free.  kTreeBlocks blocks fit the table's 64 KiB at once.
+    {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, stat_m[w][16 * c + n]);
-        const float f = (m_run[c] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[c] - M);
+        for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[blk * NS + j][n]);
+        const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) oacc[c][tt] *= f;
+        for (int tt = 0; tt < 16; ++tt) oacc[tt] *= f;
     }
     if (tid < NCOL) {
+        const int cb = tid >> 4, cn = tid & 15;
         float M = -INFINITY;
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, stat_m[w][tid]);
+        for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[cb * NS + j][cn]);
         float Ls = 0.f;
-        for (int w = 0; w < NW; ++w)
-            Ls += (stat_m[w][tid] == -INFINITY) ? 0.f : stat_l[w][tid] * __builtin_amdgcn_exp2f(stat_m[w][tid] - M);
+        for (int j = 0; j < NS; ++j) {
+            const float mj = stat_m[cb * NS + j][cn];
+            Ls += (mj == -INFINITY) ? 0.f : stat_l[cb * NS + j][cn] * __builtin_amdgcn_exp2f(mj - M);
+        }
         resM[tid] = M;
         resL[tid] = Ls;
     }
-    float4v *tree = reinterpret_cast<float4v *>(lut_mem);  // [NW/2][16][64] rows of 16 bytes <= 64 KiB
+    float4v *tree = reinterpret_cast<float4v *>(lut_mem);
+    constexpr int kTreeBlocks = (NS >= 2) ? 8 / NS : NB;  // blocks per round: [blocks][NS/2][16][64] rows
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int b0 = 0; b0 < NB; b0 += kTreeBlocks) {
+        const bool mine = blk >= b0 && blk < b0 + kTreeBlocks;
 #pragma unroll
-        for (int half = NW / 2; half >= 1; half >>= 1) {
-            if (wave_u >= half && wave_u < 2 * half) {
+        for (int half = NS / 2; half >= 1; half >>= 1) {
+            if (mine && slot >= half && slot < 2 * half) {
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt) tree[((wave_u - half) * 16 + tt) * kWave + lane] = oacc[c][tt];
+                for (int tt = 0; tt < 16; ++tt)
+                    tree[(((blk - b0) * (NS / 2) + slot - half) * 16 + tt) * kWave + lane] = oacc[tt];
             }
             __syncthreads();
-            if (wave_u < half) {
+            if (mine && slot < half) {
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt) oacc[c][tt] += tree[(wave_u * 16 + tt) * kWave + lane];
+                for (int tt = 0; tt < 16; ++tt)
+                    oacc[tt] += tree[(((blk - b0) * (NS / 2) + slot) * 16 + tt) * kWave + lane];
             }
             __syncthreads();
         }
     }
 
     if (n_active > 1) {
-        // more than one split: wave 0 leaves (M[rows], L[rows], O[rows][256]) for the combine
-        // kernel; lane (gq, n) holds dims 8 (2 (4 gq + r) + c) + i of column n in oacc[.][8 c + i][r]
-        if (wave_u == 0) {
-            const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
-            float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
-                         (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
-            if (lane < ROWS) {
-                dst[lane] = resM[lane];
-                dst[kDecStatPad + lane] = resL[lane];
-            }
+        // more than one split: the slot-0 wave of each block leaves its rows of
+        // (M[rows], L[rows], O[rows][256]) for the combine kernel; lane (gq, n) holds dims
+        // 8 (2 (4 gq + r) + c) + i of column n in oacc[8 c + i][r]
+        const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
+        float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
+                     (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
+        if (wave_u == 0 && lane < ROWS) {
+            dst[lane] = resM[lane];
+            dst[kDecStatPad + lane] = resL[lane];
+        }
+        if (slot == 0 && col < ROWS) {
+            float *row = dst + 2 * kDecStatPad + col * kDim;
 #pragma unroll
-            for (int cb = 0; cb < NC; ++cb) {
-                const int r0 = 16 * cb + n;
-                if (r0 < ROWS) {
-                    float *row = dst + 2 * kDecStatPad + r0 * kDim;
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-#pragma unroll
-                        for (int c = 0; c < 2; ++c) {
-                            const int d0 = 8 * (2 * (4 * gq + r) + c);
-                            *reinterpret_cast<float4 *>(row + d0) = make_float4(
-                                oacc[cb][8 * c][r], oacc[cb][8 * c + 1][r], oacc[cb][8 * c + 2][r], oacc[cb][8 * c + 3][r]);
-                            *reinterpret_cast<float4 *>(row + d0 + 4) = make_float4(
-                                oacc[cb][8 * c + 4][r], oacc[cb][8 * c + 5][r], oacc[cb][8 * c + 6][r], oacc[cb][8 * c + 7][r]);
-                        }
+                for (int c = 0; c < 2; ++c) {
+                    const int d0 = 8 * (2 * (4 * gq + r) + c);
+                    *reinterpret_cast<float4 *>(row + d0) =
+                        make_float4(oacc[8 * c][r], oacc[8 * c + 1][r], oacc[8 * c + 2][r], oacc[8 * c + 3][r]);
+                    *reinterpret_cast<float4 *>(row + d0 + 4) =
+                        make_float4(oacc[8 * c + 4][r], oacc[8 * c + 5][r], oacc[8 * c + 6][r], oacc[8 * c + 7][r]);
                 }
-            }
         }
         return;
     }
 
-    // ---- single split: wave 0 writes O to LDS as [row][64 quads of dims], quads swizzled within
-    // groups of 8 so both this scatter and the row reads below spread over the banks; then one
-    // wave per row applies the inverse rotation, o = H O / (256 L)
+    // ---- single split: the slot-0 waves write O to LDS as [row][64 quads of dims], quads swizzled
+    // within groups of 8 so both this scatter and the row reads below spread over the banks; then
+    // one wave per row applies the inverse rotation, o = H O / (256 L)
     auto quad_at = [](int h, int qd) { return h * 64 + (qd ^ ((h + 2 * (qd >> 4)) & 7)); };
     float4v *res4 = tree;
-    if (wave_u == 0) {
+    if (slot == 0 && col < ROWS) {
 #pragma unroll
-        for (int cb = 0; cb < NC; ++cb) {
-            const int r0 = 16 * cb + n;
-            if (r0 < ROWS) {
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) {
-                            const int qd = 16 * gq + 4 * r + 2 * c + hf;
-                            res4[quad_at(r0, qd)] =
-                                float4v{oacc[cb][8 * c + 4 * hf][r], oacc[cb][8 * c + 4 * hf + 1][r],
-                                        oacc[cb][8 * c + 4 * hf + 2][r], oacc[cb][8 * c + 4 * hf + 3][r]};
-                        }
-            }
-        }
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int qd = 16 * gq + 4 * r + 2 * c + hf;
+                    res4[quad_at(col, qd)] = float4v{oacc[8 * c + 4 * hf][r], oacc[8 * c + 4 * hf + 1][r],
+                                                     oacc[8 * c + 4 * hf + 2][r], oacc[8 * c + 4 * hf + 3][r]};
+                }
     }
     __syncthreads();
     for (int r = wave_u; r < ROWS; r += NW) {
@@ -662,13 +641,13 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStrea
     const dim3 grid(plan.n_splits, p.n_kv, p.batch);
     switch (plan.col_blocks) {
         case 1:
-            hipLaunchKernelGGL((tq4_attn_split_kernel<1, kDecWaves>), grid, dim3(kDecWaves * kWave), 0, stream, a);
+            hipLaunchKernelGGL((tq4_attn_split_kernel<1, 8>), grid, dim3(8 * kWave), 0, stream, a);
             break;
         case 2:
-            hipLaunchKernelGGL((tq4_attn_split_kernel<2, kDecWaves / 2>), grid, dim3(kDecWaves / 2 * kWave), 0, stream, a);
+            hipLaunchKernelGGL((tq4_attn_split_kernel<2, 4>), grid, dim3(8 * kWave), 0, stream, a);
             break;
         case 3:
-            hipLaunchKernelGGL((tq4_attn_split_kernel<3, kDecWaves / 2>), grid, dim3(kDecWaves / 2 * kWave), 0, stream, a);
+            hipLaunchKernelGGL((tq4_attn_split_kernel<3, 4>), grid, dim3(12 * kWave), 0, stream, a);
             break;
         default:
             return hipErrorInvalidValue;

@@ -37,7 +37,7 @@ struct DecodePlan {
     int32_t n_queries;    // query tokens per request (1: decode)
     int32_t rows;         // n_queries * group query rows per (request, KV head)
     int32_t col_blocks;   // 16-column MFMA blocks holding the rows
-    int32_t waves;        // wavefronts per split workgroup
+    int32_t slots;        // tile slots per split workgroup (wavefronts per column block)
     int32_t n_splits;     // workgroups per (request, KV head)
     int32_t split_tiles;  // 32-key tiles per workgroup
     size_t counters_bytes;
