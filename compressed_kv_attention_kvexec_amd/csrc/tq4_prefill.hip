@@ -3,11 +3,11 @@
 // Multi-query prefill reconstructs K/V tiles and runs a floating-point attention
 // consumer ("Fitting a 27B-Parameter LLM into 24 GiB of Laptop Memory", section
 // "KVExec: Fused Reconstruction with Layer-Scoped Lifetime").  Here the tiles
-// are reconstructed in the rotated domain (16 c[idx], fp16) inside registers
-// and consumed by v_mfma_f32_16x16x32_f16; the norms scale scores and
-// probabilities, and each output row gets one inverse rotation at the end
-// (KVExec row of the mechanism table in "JustFit: Run Qwen 27B Fast with its
-// full 256K context on a 24 GB Mac": attention in the rotated domain).
+// are reconstructed in the rotated domain (16 c[idx], fp16) in LDS and consumed
+// by v_mfma_f32_16x16x32_f16; the norms scale scores and probabilities, and each
+// output row gets one inverse rotation at the end (KVExec row of the mechanism
+// table in "JustFit: Run Qwen 27B Fast with its full 256K context on a 24 GB
+// Mac": attention in the rotated domain).
 //
 // Query rows of one KV head are (token, head-in-group) pairs, row = t * G + h.
 // Row r of the chunk sits at absolute position prior_len + t and sees keys
@@ -16,14 +16,16 @@
 // Three kernels per call:
 //   1. rotate: one wavefront per query row: Hq in fp32, a power-of-two scale,
 //      fp16 row and its score factor to the workspace;
-//   2. attend: grid (key split, row block, KV head); 4 wavefronts, one per
-//      SIMD, each owning R blocks of 16 rows; every wavefront walks the
-//      workgroup's key tiles, decodes each tile once and feeds its R blocks
-//      (S^T = K Q^T and O^T = V^T P^T on the same decoded operands); online
-//      softmax per row with the causal limit; a partial (O, max, sum) per row
-//      and split goes to the workspace;
+//   2. attend: grid (key split, row block, KV head); 8 wavefronts (two per
+//      SIMD), each owning R blocks of 16 rows.  The wavefronts decode each
+//      32-key tile once, together: each turns its share of the tile's indices
+//      into fp16 MFMA operands in a double-buffered LDS image, and every
+//      wavefront then feeds its blocks from that image (S^T = K Q^T,
+//      O^T = V^T P^T); online softmax per row with the causal limit; a partial
+//      (O, max, sum) per row and split goes to the workspace;
 //   3. combine: one wavefront per row: merges the splits, inverse rotation,
 //      bf16 output.
+#include <cfloat>
 #include <type_traits>
 
 #include "tq4_device.h"
@@ -32,12 +34,13 @@
 
 namespace tq4 {
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfBlocks = 2;                               // R: 16-row blocks per wavefront
+constexpr int kPfBlocks = 1;                               // R: 16-row blocks per wavefront
 constexpr int kPfRowsPerWg = kPfWaves * kPfBlocks * 16;   // 128
 constexpr int kPfPartial = kDim + 4;                       // O[256], max, sum, pad
 constexpr int kPfTargetWgs = 768;                          // 3 x 256 compute units
+constexpr int kPfAhead = 4;  // operand reads in flight ahead of the MFMAs that use them
 constexpr float kPfRescaleSlack = 8.0f;  // log2 headroom before a running maximum is moved
 
 struct PrefillArgs {
@@ -102,27 +105,107 @@ __global__ __launch_bounds__(256) void tq4_prefill_rotate_kernel(PrefillArgs a) 
 
 // ---------------------------------------------------------------- 2. attend
 
-template <int R>
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Shared tile image: the 32 fp16 MFMA operands of a 32-key tile (16 for K, 16 for V, 1 KiB each in
+// lane order) and its 64 norms, double-buffered.  Entry mt * 8 + ks is the K operand of M-tile mt,
+// K-step ks; entry 16 + c * 8 + i the V operand of M-tile (c, i) (lane layouts in tq4_tile.h).
+struct PfTileImage {
+    half8 op[32][kWave];
+    float nrm[64];  // K norms of keys 0..31, then V norms
+};
+
+template <int R, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void tq4_prefill_kernel(PrefillArgs a) {
+    constexpr int NT = NW * kWave;
+    constexpr int E = 16 / NW;  // K operands and V operands each wave decodes per tile
     __shared__ __align__(16) uint32_t lut_mem[kLutWords];
+    __shared__ __align__(16) PfTileImage img[2];
     const PrefillParams &p = a.p;
     const int G = a.group;
     const int s = blockIdx.x, rb = blockIdx.y, g = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     char *ws = static_cast<char *>(p.workspace);
 
     // rows of this wave: row0 + 16 j + n for block j
-    const int row0 = rb * kPfRowsPerWg + wave * (R * 16);
+    const int row0 = rb * kPfRowsPerWg + wave_u * (R * 16);
     const int wg_last_row = min(rb * kPfRowsPerWg + kPfRowsPerWg, a.rows) - 1;
     const int wg_kmax = p.prior_len + wg_last_row / G + 1;  // keys any row of the workgroup sees
+    const int total_keys = p.prior_len + p.chunk_len;
     const int split_keys = a.split_tiles * kTile;
     const int key_begin = s * split_keys;
     const int key_end = min(key_begin + split_keys, wg_kmax);
     const int n_tiles = key_end > key_begin ? (key_end - key_begin + kTile - 1) / kTile : 0;
 
-    // ---- per-block row data: causal limit, score factor, query operand
+    // ---- this wave's share of each tile: K operands e0 .. e0 + E - 1 and V operands
+    // 16 + e0 .. 16 + e0 + E - 1, e0 = E * wave.  K operand mt * 8 + 4 h + j is word 16 h + 4 gq + j
+    // of key 16 mt + n (E consecutive words, one load); V operand c * 8 + i comes from transposing
+    // word 2 n + c of keys sigma(0..7) (the waves with the same c share the transpose); one norm
+    // per lane (K norms in lanes 0..31, V in 32..63).
+    const int e0 = E * wave_u;
+    const int mt_w = e0 >> 3, h_w = (e0 >> 2) & 1, j_w = e0 & 3, i_w = e0 & 7;
+    const uint32_t k_lane_off = static_cast<uint32_t>(n) * 128u + static_cast<uint32_t>(gq) * 16u +
+                                2048u * mt_w + 64u * h_w + 4u * j_w;
+    const uint32_t v_lane_off = static_cast<uint32_t>(gq) * 512u + static_cast<uint32_t>(n) * 8u + 4u * mt_w;
+    const int32_t *pt = p.page_table;
+    const int pt_last = (total_keys - 1) / p.page_size;
+    using KWords = std::conditional_t<E == 4, u32x4, u32x2>;
+    struct Staging {
+        KWords k;
+        uint32_t v[8];
+        uint32_t n;
+        bool valid;
+    };
+    auto load_share = [&](Staging &st, int t) {
+        const int key0 = key_begin + t * kTile;  // t is clamped by the caller to a tile of this split
+        const int pid = pt[min(key0 / p.page_size, pt_last)];  // wave-uniform address: a scalar load
+        const int64_t rec = tile_rec0(p, g, key0, pid, st.valid);
+        const char *kb = reinterpret_cast<const char *>(p.k_words) + rec * (kWords * 4);
+        const char *vb = reinterpret_cast<const char *>(p.v_words) + rec * (kWords * 4);
+        st.k = *reinterpret_cast<const KWords *>(kb + k_lane_off);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t koff = (j < 4) ? 128u * j : 2048u + 128u * (j - 4);
+            st.v[j] = *reinterpret_cast<const uint32_t *>(vb + v_lane_off + koff);
+        }
+        const uint16_t *nb = (lane < 32 ? p.k_norms : p.v_norms) + rec + (lane & 31);
+        st.n = *nb;
+    };
+    const char *lut = reinterpret_cast<const char *>(lut_mem);
+    const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;
+    auto decode_share = [&](const Staging &st, PfTileImage &im) {
+        // all 32 table reads are issued before the first write, so the wave waits for the LDS
+        // round trip once, not once per operand
+        half8 d[2 * E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) d[j] = lut_decode(st.k[j], lane4, lut);
+        uint32_t u[8];
+        nibble_transpose8(st.v, u);
+        uint32_t uw[E];  // u[i_w .. i_w + E - 1], picked without indexing by a runtime value
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            uw[i] = u[i];
+#pragma unroll
+            for (int c = 1; c < 8 / E; ++c) uw[i] = (i_w == c * E) ? u[c * E + i] : uw[i];
+        }
+#pragma unroll
+        for (int i = 0; i < E; ++i) d[E + i] = lut_decode(uw[i], lane4, lut);
+        const float nrm = f16_bits_to_f32(static_cast<uint16_t>(st.n));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < E; ++j) im.op[e0 + j][lane] = d[j];
+#pragma unroll
+        for (int i = 0; i < E; ++i) im.op[16 + e0 + i][lane] = d[E + i];
+        im.nrm[lane] = nrm;  // every wave writes the same values
+    };
+
+    // two staging sets, each refilled in place two tiles ahead of its decode
+    Staging sa, sb;
+    load_share(sa, 0);
+
+    // ---- per-block row data: causal limit, score factor, query operand (rows past the chunk see
+    // no key and are never written)
     int lim_row[R];
     float fcol[R];
     half8 qop[R][8];
@@ -133,7 +216,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
         const int t = live ? row / G : 0;
         const int qrow = t * p.n_q + g * G + (live ? row - t * G : 0);  // index into the rotated rows
         lim_row[j] = live ? p.prior_len + t + 1 : 0;
-        fcol[j] = live ? reinterpret_cast<const float *>(ws + a.frow_off)[qrow] : 0.f;
+        fcol[j] = live ? reinterpret_cast<const float *>(ws + a.frow_off)[qrow] : 1.f;
         const char *qr = ws + a.qrot_off + static_cast<int64_t>(qrow) * (kDim * 2);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -143,12 +226,14 @@ void tq4_prefill_kernel(PrefillArgs a) {
             qop[j][ks] = __builtin_bit_cast(half8, v);
         }
     }
-    build_lut<kPfThreads>(lut_mem, a.lut_pairs, tid);
+    build_lut<NT>(lut_mem, a.lut_pairs, tid);
     __syncthreads();
-    const char *lut = reinterpret_cast<const char *>(lut_mem);
-    const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;
-    const LaneOffsets lofs = lane_offsets(lane);
-    const int32_t *pt = p.page_table;
+    const int t_last = max(n_tiles - 1, 0);
+    decode_share(sa, img[0]);
+    bool valid0 = sa.valid, valid1 = false;  // tiles in img[0] and img[1]
+    load_share(sb, min(1, t_last));
+    load_share(sa, min(2, t_last));
+    __syncthreads();
 
     float4v oacc[R][16];
     float m_run[R], l_run[R];
@@ -160,87 +245,81 @@ void tq4_prefill_kernel(PrefillArgs a) {
         l_run[j] = 0.f;
     }
 
-    KRegs kr;
-    VRegs vr;
-    bool valid_cur = false, valid_next = false;
-    int64_t rec_next = 0;
-    auto rec_of = [&](int t, bool &valid_d) -> int64_t {
+    // Tiles in pairs: decode this wave's share of tile t + 1 into the other buffer, request its share
+    // of tile t + 3 into the staging set just consumed, then run all R blocks on tile t from the
+    // shared image; one barrier per tile.  A pair's second tile past the end is computed fully
+    // masked (its image holds a clamped, valid tile), which keeps every wave's loads and barriers
+    // the same.
+    auto compute = [&](const PfTileImage &im, int t, bool valid) {
         const int key0 = key_begin + t * kTile;
-        const int pid = pt[key0 / p.page_size];  // wave-uniform address: a scalar load
-        return tile_rec0(p, g, key0, pid, valid_d);
-    };
-    if (n_tiles > 0) {
-        rec_next = rec_of(0, valid_next);
-        load_k(p, rec_next, lofs, kr);
-        load_v(p, rec_next, lofs, vr);
-    }
-
-    auto step = [&](int t, auto prefetch) {
-        const int key0 = key_begin + t * kTile;
-        const bool valid = valid_cur;
-        // ---- scores for all R blocks from one decode of the K tile
+        // ---- scores for all R blocks.  Operands are read kPfAhead entries ahead of their MFMAs
+        // and the order is pinned, so only a few operands are live at once (the compiler would
+        // otherwise hoist all 16 reads and run out of registers).
         float4v sacc[R][2];
 #pragma unroll
         for (int j = 0; j < R; ++j) sacc[j][0] = sacc[j][1] = float4v{0.f, 0.f, 0.f, 0.f};
+        half8 opb[kPfAhead + 1];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int e = 0; e < kPfAhead; ++e) opb[e] = im.op[e][lane];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const u32x4 kw = kr.k[mt][ks >> 2];
-                const uint32_t w = (ks & 3) == 0 ? kw.x : (ks & 3) == 1 ? kw.y : (ks & 3) == 2 ? kw.z : kw.w;
-                const half8 kop = lut_decode(w, lane4, lut);
+        for (int e = 0; e < 16; ++e) {
+            if (e + kPfAhead < 16) opb[(e + kPfAhead) % (kPfAhead + 1)] = im.op[e + kPfAhead][lane];
 #pragma unroll
-                for (int j = 0; j < R; ++j)
-                    sacc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[j][ks], sacc[j][mt], 0, 0, 0);
-            }
-        float kn[8], nv[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            kn[4 * h + 0] = f16lo(kr.kn[h].x);
-            kn[4 * h + 1] = f16hi(kr.kn[h].x);
-            kn[4 * h + 2] = f16lo(kr.kn[h].y);
-            kn[4 * h + 3] = f16hi(kr.kn[h].y);
-            nv[4 * h + 0] = f16lo(vr.vn[h].x);
-            nv[4 * h + 1] = f16hi(vr.vn[h].x);
-            nv[4 * h + 2] = f16lo(vr.vn[h].y);
-            nv[4 * h + 3] = f16hi(vr.vn[h].y);
-        }
-        if constexpr (decltype(prefetch)::value) {
-            rec_next = rec_of(t + 1, valid_next);
-            __builtin_amdgcn_sched_barrier(0);
-            load_k(p, rec_next, lofs, kr);
+            for (int j = 0; j < R; ++j)
+                sacc[j][e >> 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(opb[e % (kPfAhead + 1)], qop[j][e & 7],
+                                                                         sacc[j][e >> 3], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the first V operands are requested before the softmax
+#pragma unroll
+        for (int e = 0; e < kPfAhead; ++e) opb[e] = im.op[16 + e][lane];
+        // lane holds keys sigma(j): j < 4 -> 4 gq + j, else 16 + 4 gq + j - 4
+        const float4 kn0 = *reinterpret_cast<const float4 *>(&im.nrm[4 * gq]);
+        const float4 kn1 = *reinterpret_cast<const float4 *>(&im.nrm[16 + 4 * gq]);
+        const float4 nv0 = *reinterpret_cast<const float4 *>(&im.nrm[32 + 4 * gq]);
+        const float4 nv1 = *reinterpret_cast<const float4 *>(&im.nrm[48 + 4 * gq]);
+        const float kn[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
+        const float nv[8] = {nv0.x, nv0.y, nv0.z, nv0.w, nv1.x, nv1.y, nv1.z, nv1.w};
         // ---- online softmax per block, probabilities as the P^T operand
         half8 pop[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int lim = valid ? min(key_end, lim_row[j]) - key0 : 0;  // visible keys in this tile
-            float sc[8];
+            float xs[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int koff = (q < 4) ? (4 * gq + q) : (16 + 4 * gq + (q - 4));
-                sc[q] = (koff < lim) ? sacc[j][q >> 2][q & 3] * kn[q] * fcol[j] : -INFINITY;
+                xs[q] = (koff < lim) ? sacc[j][q >> 2][q & 3] * kn[q] : -INFINITY;
             }
-            float mx = sc[0];
+            float mx = xs[0];
 #pragma unroll
-            for (int q = 1; q < 8; ++q) mx = fmaxf(mx, sc[q]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            for (int q = 1; q < 8; ++q) mx = fmaxf(mx, xs[q]);
+            float lo, hi;  // row n's maximum over the four lane groups
+            lane_pair<16>(mx, lo, hi);
+            mx = fmaxf(lo, hi);
+            lane_pair<32>(mx, lo, hi);
+            mx = fmaxf(lo, hi) * fcol[j];  // fcol > 0
             // the reference maximum moves only when a score exceeds it by more than the slack
             // (exp2(s - m_run) <= 256 stays well inside fp16), so rescaling is rare
             if (__any(mx > m_run[j] + kPfRescaleSlack)) {
                 const float m_new = fmaxf(m_run[j], mx);
                 const float alpha = (m_new > m_run[j]) ? __builtin_amdgcn_exp2f(m_run[j] - m_new) : 1.0f;
                 l_run[j] *= alpha;
+                // one accumulator tile at a time (the path is rare; this keeps its registers few)
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt) oacc[j][tt] *= alpha;
+                for (int tt = 0; tt < 16; ++tt) {
+                    oacc[j][tt] *= alpha;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 m_run[j] = m_new;
             }
+            // m_run is -inf only while every key of the row so far was masked; the floor keeps
+            // fcol x - m finite or -inf then, and exp2(-inf) = 0 drops masked keys
+            const float neg_m = -fmaxf(m_run[j], -FLT_MAX);
             float pv[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const float e = (sc[q] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[q] - m_run[j]);
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[q], fcol[j], neg_m));
                 l_run[j] += e;
                 pv[q] = e * nv[q];
             }
@@ -251,31 +330,29 @@ void tq4_prefill_kernel(PrefillArgs a) {
             pr.w = pack_f16x2(pv[6], pv[7]);
             pop[j] = __builtin_bit_cast(half8, pr);
         }
-        // ---- O^T += V^T P^T for all R blocks from one decode of the V tile
+        // ---- O^T += V^T P^T for all R blocks, operands pipelined as for the scores
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            uint32_t wv[8], u[8];
+        for (int e = 0; e < 16; ++e) {
+            if (e + kPfAhead < 16) opb[(e + kPfAhead) % (kPfAhead + 1)] = im.op[16 + e + kPfAhead][lane];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) wv[q] = c == 0 ? vr.v[q].x : vr.v[q].y;
-            nibble_transpose8(wv, u);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const half8 vop = lut_decode(u[i], lane4, lut);
-#pragma unroll
-                for (int j = 0; j < R; ++j)
-                    oacc[j][8 * c + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[j], oacc[j][8 * c + i], 0, 0, 0);
-            }
-        }
-        if constexpr (decltype(prefetch)::value) {
-            __builtin_amdgcn_sched_barrier(0);
-            load_v(p, rec_next, lofs, vr);
+            for (int j = 0; j < R; ++j)
+                oacc[j][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(opb[e % (kPfAhead + 1)], pop[j], oacc[j][e], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        valid_cur = valid_next;
     };
-    valid_cur = valid_next;
-    for (int t = 0; t + 1 < n_tiles; ++t) step(t, std::true_type{});
-    if (n_tiles > 0) step(n_tiles - 1, std::false_type{});
+    for (int t = 0; t < n_tiles; t += 2) {
+        decode_share(sb, img[1]);
+        valid1 = sb.valid;
+        load_share(sb, min(t + 3, t_last));
+        compute(img[0], t, valid0);
+        __syncthreads();
+        decode_share(sa, img[0]);
+        valid0 = sa.valid;
+        load_share(sa, min(t + 4, t_last));
+        compute(img[1], t + 1, valid1 && t + 1 < n_tiles);
+        __syncthreads();
+    }
 
     // ---- partials: lane (gq, n) of block j holds row n, dims 8 (2 (4 gq + r) + c) + i
     float *parts = reinterpret_cast<float *>(ws + a.parts_off);
@@ -351,7 +428,7 @@ hipError_t launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipSt
     const int64_t comb_blocks = (static_cast<int64_t>(p.n_kv) * a.rows + 3) / 4;
     if (rot_blocks > 0x7fffffff || comb_blocks > 0x7fffffff || plan.n_qblocks > 65535) return hipErrorInvalidValue;
     hipLaunchKernelGGL(tq4_prefill_rotate_kernel, dim3(static_cast<unsigned>(rot_blocks)), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(tq4_prefill_kernel<kPfBlocks>, dim3(plan.n_splits, plan.n_qblocks, p.n_kv), dim3(kPfThreads),
+    hipLaunchKernelGGL((tq4_prefill_kernel<kPfBlocks, kPfWaves>), dim3(plan.n_splits, plan.n_qblocks, p.n_kv), dim3(kPfThreads),
                        0, stream, a);
     hipLaunchKernelGGL(tq4_prefill_combine_kernel, dim3(static_cast<unsigned>(comb_blocks)), dim3(256), 0, stream, a);
     return hipGetLastError();
