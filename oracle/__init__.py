@@ -79,6 +79,12 @@ def _load():
                                    c_f64p, i32, i32, c_i32p, i32, c_i32p, c_i32p,
                                    ctypes.c_double, i32, i32, c_f64p]
     lib.tq4o_attention.restype = ctypes.c_int
+    lib.tq4o_f64_to_bf16_array.argtypes = [c_f64p, c_u16p, i64]
+    lib.tq4o_reconstruct.argtypes = [c_u32p, c_u16p, c_u32p, c_u16p, i32, i32, i32, c_i32p, i32, c_i32p,
+                                     i32, i32, c_u16p, c_u16p]
+    lib.tq4o_reconstruct.restype = ctypes.c_int
+    lib.tq4o_sdpa_dense.argtypes = [c_f64p, c_f64p, c_f64p, i32, i32, i32, i32, c_i32p, ctypes.c_double, c_f64p]
+    lib.tq4o_sdpa_dense.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -299,6 +305,64 @@ def attn_prefill_rows(pool: Pool, q_rows, rows, page_table_row, prior_len: int, 
     rows = np.asarray(rows, np.int32)
     return attention(pool, q_rows, np.asarray(page_table_row, np.int32)[None, :],
                      np.zeros(len(rows), np.int32), prior_len + rows + 1, scale, heads)
+
+
+# --------------------------------------------------------------------------
+# Unfused path (section "KVExec: Fused Reconstruction with Layer-Scoped
+# Lifetime": reconstruction into contiguous query-dtype K/V, then SDPA)
+# --------------------------------------------------------------------------
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round fp64 values to bf16 (nearest, ties to even) in one step; uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, np.uint16)
+    _load().tq4o_f64_to_bf16_array(_ptr(x.reshape(-1), ctypes.c_double),
+                                   _ptr(out.reshape(-1), ctypes.c_uint16), x.size)
+    return out
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bits -> exact fp64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def reconstruct(pool: Pool, page_table, seq_lens, max_seq_len: int):
+    """bf16 bits of K and V, [batch][n_kv][max_seq_len][256]: position p < seq_lens[b] (clamped) of
+    request b is the exact decode of its record rounded to bf16; later positions stay 0."""
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    if pt.ndim == 1:
+        pt = pt[None, :]
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    batch = lens.shape[0]
+    k = np.zeros((batch, pool.n_kv, max_seq_len, DIM), np.uint16)
+    v = np.zeros_like(k)
+    rc = _load().tq4o_reconstruct(
+        _ptr(pool.k_words, ctypes.c_uint32), _ptr(pool.k_norms, ctypes.c_uint16),
+        _ptr(pool.v_words, ctypes.c_uint32), _ptr(pool.v_norms, ctypes.c_uint16),
+        pool.num_pages, pool.n_kv, pool.page_size, _ptr(pt, ctypes.c_int32), pt.shape[1],
+        _ptr(lens, ctypes.c_int32), batch, int(max_seq_len), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError("page ID outside the pool")
+    return k, v
+
+
+def sdpa_dense(q, k, v, seq_lens, scale: float) -> np.ndarray:
+    """fp64 attention of q [batch][n_q][256] over dense k, v [batch][n_kv][S][256] (any real dtype,
+    taken exactly), keys 0 .. seq_lens[b] - 1 (clamped to [0, S])."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    batch, n_q, _ = q.shape
+    n_kv, S = k.shape[1], k.shape[2]
+    out = np.zeros((batch, n_q, DIM), np.float64)
+    rc = _load().tq4o_sdpa_dense(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                                 batch, n_q, n_kv, S, _ptr(lens, ctypes.c_int32), float(scale),
+                                 _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise MemoryError("oracle sdpa_dense")
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -384,6 +384,116 @@ int tq4o_attention(const uint32_t *k_words, const uint16_t *k_norms, const uint3
 }
 
 /* ------------------------------------------------------------------------ */
+/* Unfused path: reconstruct K/V into the query dtype, then dense attention. */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * fp64 -> bf16 bits, round to nearest, ties to even, taken in one step from the
+ * fp64 value (no intermediate fp32 rounding).  bf16 keeps 8 significant bits and
+ * fp32's exponent range; below 2^-126 its spacing is 2^-133.  Values whose
+ * magnitude rounds to 2^128 or more become infinity.  NaN maps to a quiet NaN.
+ */
+uint16_t tq4o_f64_to_bf16(double x) {
+    if (isnan(x)) return 0x7fc0;
+    const int neg = signbit(x) ? 1 : 0;
+    double a = fabs(x);
+    uint16_t sign = (uint16_t)(neg << 15);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                     /* a = m 2^e, m in [0.5, 1) */
+    int qexp = e - 8;                 /* spacing of 8-bit significands in [2^(e-1), 2^e) */
+    if (qexp < -133) qexp = -133;     /* subnormal spacing */
+    const double r = rint(ldexp(a, -qexp));   /* exact scaling; rint rounds half to even */
+    const double v = ldexp(r, qexp);
+    if (v >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7f80);
+    const float f = (float)v;         /* exact: v has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    return (uint16_t)(sign | ((bits >> 16) & 0x7fff));
+}
+
+/*
+ * Reconstruction into contiguous K/V ([KVX]: multi-query prefill can reconstruct
+ * the pages into contiguous tensors of the query dtype, and a gather-and-SDPA
+ * path is the fallback).  For request b, KV head g and position p < L_b
+ * (L_b = seq_lens[b] clamped to [0, max_seq]): out[b][g][p][:] = bf16(decode of
+ * the record at page_table[b][p / P], offset p % P).  Positions p >= L_b are not
+ * written.  Outputs are bf16 bits [batch][n_kv][max_seq][256].  Returns 0, or -1
+ * on a page ID outside the pool.
+ */
+int tq4o_reconstruct(const uint32_t *k_words, const uint16_t *k_norms, const uint32_t *v_words,
+                     const uint16_t *v_norms, int32_t num_pages, int32_t n_kv, int32_t P,
+                     const int32_t *page_table, int32_t table_stride, const int32_t *seq_lens,
+                     int32_t batch, int32_t max_seq, uint16_t *k_out, uint16_t *v_out) {
+    double x[TQ4O_DIM];
+    for (int32_t b = 0; b < batch; ++b) {
+        int32_t L = seq_lens[b];
+        if (L < 0) L = 0;
+        if (L > max_seq) L = max_seq;
+        for (int32_t g = 0; g < n_kv; ++g) {
+            for (int32_t p = 0; p < L; ++p) {
+                const int32_t page = page_table[(size_t)b * table_stride + p / P];
+                if (page < 0 || page >= num_pages) return -1;
+                const size_t rec = rec_index(page, g, p % P, n_kv, P);
+                const size_t o = (((size_t)b * n_kv + g) * max_seq + p) * TQ4O_DIM;
+                tq4o_decode_vec(k_words + rec * TQ4O_WORDS, k_norms[rec], x);
+                for (int d = 0; d < TQ4O_DIM; ++d) k_out[o + d] = tq4o_f64_to_bf16(x[d]);
+                tq4o_decode_vec(v_words + rec * TQ4O_WORDS, v_norms[rec], x);
+                for (int d = 0; d < TQ4O_DIM; ++d) v_out[o + d] = tq4o_f64_to_bf16(x[d]);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Dense scaled dot-product attention for one query per request over contiguous
+ * K/V in fp64: q [batch][n_q][256], k and v [batch][n_kv][max_seq][256], keys
+ * 0 .. L_b - 1 (L_b = seq_lens[b] clamped to [0, max_seq]); query head h reads
+ * KV head h / (n_q / n_kv).  out [batch][n_q][256]; a request with L_b = 0 gets
+ * zeros.  Returns 0, or -2 when memory runs out.
+ */
+int tq4o_sdpa_dense(const double *q, const double *k, const double *v, int32_t batch, int32_t n_q,
+                    int32_t n_kv, int32_t max_seq, const int32_t *seq_lens, double scale, double *out) {
+    const int32_t group = n_q / n_kv;
+    double *s = (double *)malloc((size_t)(max_seq > 0 ? max_seq : 1) * sizeof(double));
+    if (!s) return -2;
+    for (int32_t b = 0; b < batch; ++b) {
+        int32_t L = seq_lens[b];
+        if (L < 0) L = 0;
+        if (L > max_seq) L = max_seq;
+        for (int32_t h = 0; h < n_q; ++h) {
+            const int32_t g = h / group;
+            const double *qh = q + ((size_t)b * n_q + h) * TQ4O_DIM;
+            const double *kb = k + ((size_t)b * n_kv + g) * max_seq * TQ4O_DIM;
+            const double *vb = v + ((size_t)b * n_kv + g) * max_seq * TQ4O_DIM;
+            double *oh = out + ((size_t)b * n_q + h) * TQ4O_DIM;
+            for (int d = 0; d < TQ4O_DIM; ++d) oh[d] = 0.0;
+            if (L == 0) continue;
+            double mx = -INFINITY;
+            for (int32_t j = 0; j < L; ++j) {
+                double dot = 0.0;
+                for (int d = 0; d < TQ4O_DIM; ++d) dot += qh[d] * kb[(size_t)j * TQ4O_DIM + d];
+                s[j] = scale * dot;
+                if (s[j] > mx) mx = s[j];
+            }
+            double sum = 0.0;
+            for (int32_t j = 0; j < L; ++j) { s[j] = exp(s[j] - mx); sum += s[j]; }
+            for (int32_t j = 0; j < L; ++j) {
+                const double pj = s[j] / sum;
+                for (int d = 0; d < TQ4O_DIM; ++d) oh[d] += pj * vb[(size_t)j * TQ4O_DIM + d];
+            }
+        }
+    }
+    free(s);
+    return 0;
+}
+
+void tq4o_f64_to_bf16_array(const double *in, uint16_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = tq4o_f64_to_bf16(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array conveniences for the Python wrapper (loops over the above).        */
 /* ------------------------------------------------------------------------ */
 
