@@ -215,6 +215,66 @@ def decode_config_leg(name: str, device, reps: int = 20, n_queries: int = 1) -> 
     return r
 
 
+def unfused_leg(device, reps: int = 10) -> dict:
+    """The unfused path on one layer of the 212,992-position workload, timed cold: reconstruct the
+    pages into bf16 K/V (tq4_reconstruct_pages), then dense decode attention over them
+    (tq4_sdpa_decode).  Reports each call, the sum, and the bytes the reconstruction materialises."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    import synth
+    w = synth.WORKLOADS["decode_212k_16l"]
+    table = synth.placement(w, 0)
+    slots = synth.used_slots(w, table)
+    pool = tq4.Tq4LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+    sd = torch.from_numpy(slots).to(device)
+    for which, st in ((0, synth.T_K), (1, synth.T_V)):
+        src = synth.torch_normal(synth.seed_of(w.wid, 0, st), (len(slots), w.n_kv, 256), device)
+        for c in range(0, len(slots), 65536):
+            part = src[c:c + 65536]
+            tq4.tq4_encode_pages(pool, part if which == 0 else None, part if which == 1 else None,
+                                 sd[c:c + 65536])
+        del src
+    L = w.seq_lens[0]
+    q = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (1, w.n_q, 256), device).to(torch.bfloat16)
+    tab = torch.from_numpy(table).to(device)
+    seq = torch.tensor([L], dtype=torch.int32, device=device)
+    k = torch.empty((1, w.n_kv, L, 256), dtype=torch.bfloat16, device=device)
+    v = torch.empty_like(k)
+    out = torch.empty_like(q)
+    ws = tq4.new_workspace(tq4.tq4_sdpa_decode_workspace_size(1, L, w.n_q, w.n_kv), device)
+    rec = tq4.prepare_reconstruct(pool, tab, seq, L, k, v)
+    att = tq4.prepare_sdpa_decode(q, k, v, seq, synth.SCALE, out, ws)
+    flush = torch.ones(192 << 20, dtype=torch.float32, device=device)
+    for _ in range(2):
+        rec()
+        att()
+    t_rec, t_att = [], []
+    for _ in range(reps):
+        flush.sum()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        rec()
+        e[1].record()
+        att()
+        e[2].record()
+        torch.cuda.synchronize()
+        t_rec.append(e[0].elapsed_time(e[1]) / 1e3)
+        t_att.append(e[1].elapsed_time(e[2]) / 1e3)
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite unfused output")
+    tr, ta = sorted(t_rec)[reps // 2], sorted(t_att)[reps // 2]
+    kv_bytes = 2 * w.n_kv * L * 256 * 2
+    tq4_bytes = L * TQ4_BYTES_PER_POS_LAYER
+    del pool, k, v, flush
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "layers": 1, "cached_positions": L,
+            "reconstruct_us": tr * 1e6, "sdpa_us": ta * 1e6, "total_us": (tr + ta) * 1e6,
+            "materialized_bf16_kv_bytes": kv_bytes,
+            "reconstruct_gb_per_s": (tq4_bytes + kv_bytes) / tr / 1e9,
+            "sdpa_gb_per_s": (kv_bytes + 2 * w.n_q * 256 * 2) / ta / 1e9,
+            "timing": f"median of {reps} cold calls (768 MiB read before each pair)"}
+
+
 def prefill_leg(device, reps: int = 3):
     """The chunked-prefill workload: 2,048 bf16 query tokens x 24 heads over 194,560 cached
     positions plus the chunk itself (causal inside the chunk), one layer.  Reports the call
@@ -318,6 +378,8 @@ def main() -> int:
                     help="skip the one-layer cold timings of the other decode workloads")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the one-layer cold timings of the packed multi-query verifier")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the reconstruct-then-dense-attention timing")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager per-layer launches instead of a HIP graph of the step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -476,6 +538,14 @@ def main() -> int:
             result["extra"]["verify"].append(r)
             log(f"verify k={k} at {w.seq_lens}: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s, "
                 f"{r['tflops']:.1f} TFLOP/s (cold)")
+    if not args.no_unfused:
+        r = unfused_leg(dev)
+        r["fused_call_us"] = result["roofline"]["avg_launch_us"]
+        r["unfused_over_fused"] = r["total_us"] / r["fused_call_us"]
+        result["extra"]["unfused"] = r
+        log(f"unfused: reconstruct {r['reconstruct_us']:.1f} us + dense attention {r['sdpa_us']:.1f} us "
+            f"= {r['total_us']:.1f} us ({r['unfused_over_fused']:.1f}x the fused call), "
+            f"{r['materialized_bf16_kv_bytes'] / 2**20:.0f} MiB of bf16 K/V")
     if not args.no_prefill:
         log("prefill leg ...")
         result["extra"]["prefill"] = prefill_leg(dev)

@@ -23,7 +23,8 @@ __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_e
            "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library",
            "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill",
            "tq4_attn_decode_append", "prepare_decode_append", "tq4_attn_verify_workspace_size",
-           "tq4_attn_verify", "prepare_verify"]
+           "tq4_attn_verify", "prepare_verify", "tq4_reconstruct_pages", "tq4_sdpa_decode_workspace_size",
+           "tq4_sdpa_decode", "prepare_reconstruct", "prepare_sdpa_decode"]
 
 HEAD_DIM = 256
 WORDS = 32
@@ -187,6 +188,44 @@ def tq4_attn_verify(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tenso
     return out
 
 
+def tq4_reconstruct_pages(pool: Tq4LayerPool, page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                          k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None, stream=None):
+    """bf16 K and V [batch][n_kv][max_seq_len][256] of every cached position (rows past a request's
+    length are left as they were)."""
+    batch = int(seq_lens.shape[0])
+    shape = (batch, pool.n_kv, int(max_seq_len), HEAD_DIM)
+    dev = pool.k_words.device
+    if k_out is None:
+        k_out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    if v_out is None:
+        v_out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    ps = pool.struct()
+    check(load_library().tq4_reconstruct_pages(
+        ctypes.byref(ps), _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len),
+        _dtype_code(k_out), _ptr(k_out), _ptr(v_out), _stream(stream)))
+    return k_out, v_out
+
+
+def tq4_sdpa_decode_workspace_size(batch: int, max_seq_len: int, n_q_heads: int, n_kv_heads: int) -> int:
+    return int(load_library().tq4_sdpa_decode_workspace_size(batch, max_seq_len, n_q_heads, n_kv_heads))
+
+
+def tq4_sdpa_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """q [batch][n_q][256] bf16 over dense k, v [batch][n_kv][max_seq_len][256] bf16."""
+    batch, n_q, _ = q.shape
+    n_kv, max_seq = int(k.shape[1]), int(k.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_sdpa_decode_workspace_size(batch, max_seq, n_q, n_kv), q.device)
+    check(load_library().tq4_sdpa_decode(
+        _ptr(q), _dtype_code(q), _ptr(k), _ptr(v), _dtype_code(k), _ptr(seq_lens), batch, max_seq, n_q, n_kv,
+        float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def tq4_attn_prefill_chunk(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor,
                            prior_len: int, scale: float, out: torch.Tensor | None = None,
                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
@@ -249,6 +288,23 @@ def prepare_verify(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor
             _ptr(seq_lens), batch, int(max_seq_len), n_q, ctypes.c_float(scale), _ptr(out),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     return PreparedCall(load_library().tq4_attn_verify, args, (ps, pool, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_reconstruct(pool: Tq4LayerPool, page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                        k_out: torch.Tensor, v_out: torch.Tensor, stream=None) -> PreparedCall:
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), int(seq_lens.shape[0]),
+            int(max_seq_len), _dtype_code(k_out), _ptr(k_out), _ptr(v_out), _stream(stream))
+    return PreparedCall(load_library().tq4_reconstruct_pages, args, (ps, pool, page_table, seq_lens, k_out, v_out))
+
+
+def prepare_sdpa_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                        out: torch.Tensor, workspace: torch.Tensor, stream=None) -> PreparedCall:
+    batch, n_q, _ = q.shape
+    args = (_ptr(q), _dtype_code(q), _ptr(k), _ptr(v), _dtype_code(k), _ptr(seq_lens), batch, int(k.shape[2]), n_q,
+            int(k.shape[1]), ctypes.c_float(scale), _ptr(out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    return PreparedCall(load_library().tq4_sdpa_decode, args, (q, k, v, seq_lens, out, workspace))
 
 
 def prepare_prefill(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, prior_len: int,

@@ -67,6 +67,12 @@ def load_library(path: str | None = None):
     lib.tq4_attn_verify_workspace_size.restype = sz
     lib.tq4_attn_verify.argtypes = [pool_p, vp, st, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
     lib.tq4_attn_verify.restype = st
+    lib.tq4_reconstruct_pages.argtypes = [pool_p, vp, i32, vp, i32, i32, st, vp, vp, vp]
+    lib.tq4_reconstruct_pages.restype = st
+    lib.tq4_sdpa_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.tq4_sdpa_decode_workspace_size.restype = sz
+    lib.tq4_sdpa_decode.argtypes = [vp, st, vp, vp, st, vp, i32, i32, i32, i32, f32, vp, vp, sz, vp]
+    lib.tq4_sdpa_decode.restype = st
     lib.tq4_attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.tq4_attn_prefill_workspace_size.restype = sz
     lib.tq4_attn_prefill_chunk.argtypes = [pool_p, vp, st, vp, i32, i32, i32, f32, vp, vp, sz, vp]

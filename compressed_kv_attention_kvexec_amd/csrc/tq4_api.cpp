@@ -204,6 +204,74 @@ tq4_status tq4_attn_decode_append(const tq4_layer_pool *pool, const void *k_new,
                          workspace_bytes, stream);
 }
 
+tq4_status tq4_reconstruct_pages(const tq4_layer_pool *pool, const int32_t *page_table, int32_t page_table_stride,
+                                 const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, tq4_dtype out_dtype,
+                                 void *k_out, void *v_out, void *stream) {
+    tq4_status st = check_pool(pool);
+    if (st != TQ4_OK) return st;
+    if ((st = check_pool_reads(pool)) != TQ4_OK) return st;
+    if (!page_table || !seq_lens || !k_out || !v_out) return TQ4_ERR_NULL;
+    if (out_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
+    if (batch < 1 || batch > 65535 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
+    if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
+    if (!aligned(k_out, 16) || !aligned(v_out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return TQ4_ERR_ALIGN;
+    tq4::ReconParams p{};
+    p.k_words = pool->k_words;
+    p.v_words = pool->v_words;
+    p.k_norms = pool->k_norms;
+    p.v_norms = pool->v_norms;
+    p.num_pages = pool->num_pages;
+    p.page_size = pool->page_size;
+    p.n_kv = pool->n_kv_heads;
+    p.page_table = page_table;
+    p.table_stride = page_table_stride;
+    p.seq_lens = seq_lens;
+    p.batch = batch;
+    p.max_seq_len = max_seq_len;
+    p.k_out = static_cast<uint16_t *>(k_out);
+    p.v_out = static_cast<uint16_t *>(v_out);
+    return from_hip(tq4::launch_reconstruct(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t tq4_sdpa_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads) {
+    if (batch < 1 || max_seq_len < 1 || n_kv_heads < 1) return 0;
+    if (check_heads(n_q_heads, n_kv_heads) != TQ4_OK) return 0;
+    return tq4::plan_dense(batch, max_seq_len, n_q_heads, n_kv_heads).workspace_bytes;
+}
+
+tq4_status tq4_sdpa_decode(const void *q, tq4_dtype q_dtype, const void *k, const void *v, tq4_dtype kv_dtype,
+                           const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                           int32_t n_kv_heads, float scale, void *out, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    if (!q || !k || !v || !seq_lens || !out) return TQ4_ERR_NULL;
+    if (q_dtype != TQ4_BF16 || kv_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
+    if (n_kv_heads < 1 || n_kv_heads > 65535) return TQ4_ERR_SHAPE;
+    tq4_status st = check_heads(n_q_heads, n_kv_heads);
+    if (st != TQ4_OK) return st;
+    if (batch < 1 || batch > 65535 || max_seq_len < 1) return TQ4_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
+        return TQ4_ERR_ALIGN;
+    const tq4::DensePlan plan = tq4::plan_dense(batch, max_seq_len, n_q_heads, n_kv_heads);
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return TQ4_ERR_WORKSPACE;
+    if (workspace != nullptr && !aligned(workspace, 256)) return TQ4_ERR_ALIGN;
+    tq4::DenseParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.seq_lens = seq_lens;
+    p.out = static_cast<uint16_t *>(out);
+    p.workspace = workspace;
+    p.batch = batch;
+    p.max_seq_len = max_seq_len;
+    p.n_q = n_q_heads;
+    p.n_kv = n_kv_heads;
+    p.scale = scale;
+    return from_hip(tq4::launch_dense(p, plan, static_cast<hipStream_t>(stream)));
+}
+
 size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,
                                        int32_t n_kv_heads, int32_t page_size) {
     if (prior_len < 0 || chunk_len < 1 || n_kv_heads < 1) return 0;

@@ -41,9 +41,6 @@ constexpr int kPlanWgsPerCU = 1;    // resident decode workgroups per CU
 constexpr int kMinTilesPerWave = 2;
 constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running maximum is moved
 
-constexpr int kDecStatPad = 64;
-  // floats of each statistic row in a split partial (rows <= 64)
-
 struct DecodeArgs {
     DecodeParams p;
     int32_t group;
@@ -76,8 +73,8 @@ DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, in
     pl.split_tiles = static_cast<int32_t>((tiles + want - 1) / want);
     pl.n_splits = static_cast<int32_t>((tiles + pl.split_tiles - 1) / pl.split_tiles);
     pl.counters_bytes = 0;
-    // per split: M[rows] and L[rows], each padded to kDecStatPad floats, then O[rows][256]
-    pl.partial_floats = 2 * kDecStatPad + static_cast<size_t>(pl.rows) * kDim;
+    // per split: M[rows] and L[rows], each padded to kSplitStatPad floats, then O[rows][256]
+    pl.partial_floats = 2 * kSplitStatPad + static_cast<size_t>(pl.rows) * kDim;
     // one partial per (request, KV head, split); nothing when there is a single split
     pl.workspace_bytes = pl.n_splits > 1 ? static_cast<size_t>(units) * pl.n_splits * pl.partial_floats * sizeof(float)
                                          : 0;
@@ -470,10 +467,10 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
                      (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
         if (wave_u == 0 && lane < ROWS) {
             dst[lane] = resM[lane];
-            dst[kDecStatPad + lane] = resL[lane];
+            dst[kSplitStatPad + lane] = resL[lane];
         }
         if (slot == 0 && col < ROWS) {
-            float *row = dst + 2 * kDecStatPad + col * kDim;
+            float *row = dst + 2 * kSplitStatPad + col * kDim;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -543,20 +540,19 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(DecodeArgs a) {
+template <bool kRotated>
+__global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(CombineArgs a) {
     __shared__ float4v part[kCombWaves][kWave];
-    const DecodeParams &p = a.p;
     const int G = a.group;
     const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int L_req = p.seq_lens[b];
+    const int L_req = a.seq_lens[b];
     const size_t pf = static_cast<size_t>(a.partial_floats);
-    const float *base = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + a.parts_off) +
-                        (static_cast<size_t>(b) * p.n_kv + g) * a.n_splits * pf;
+    const float *base = a.parts + (static_cast<size_t>(b) * a.n_kv + g) * a.n_splits * pf;
     const float *mrow = base + r;
-    const float *lrow = base + kDecStatPad + r;
-    const float *orow = base + 2 * kDecStatPad + static_cast<size_t>(r) * kDim + 4 * lane;
+    const float *lrow = base + kSplitStatPad + r;
+    const float *orow = base + 2 * kSplitStatPad + static_cast<size_t>(r) * kDim + 4 * lane;
     const int ns = a.n_splits;
     // Every load of the first group of 64 splits is issued before the length is known (slots past
     // the live splits hold stale data and are dropped by selection, never multiplied in).
@@ -569,7 +565,7 @@ __global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(Decode
         const int s = min(wave + kCombWaves * u, ns - 1);
         v[u] = *reinterpret_cast<const float4v *>(orow + s * pf);
     }
-    const int L = L_req < 0 ? 0 : (L_req > p.max_seq_len ? p.max_seq_len : L_req);
+    const int L = L_req < 0 ? 0 : (L_req > a.max_seq_len ? a.max_seq_len : L_req);
     const int split_keys = a.split_tiles * kTile;
     const int n_active = (L + split_keys - 1) / split_keys;
     // With one live split the split kernel wrote this output itself; such a request still runs
@@ -614,16 +610,28 @@ __global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(Decode
     if (wave == 0 && merge) {
         const float4v t = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
         float y[4] = {t[0], t[1], t[2], t[3]};
-        wave_fwht(y, lane);
-        const float f = Ltot > 0.f ? (1.0f / 256.0f) / Ltot : 0.f;
+        float f = Ltot > 0.f ? 1.0f / Ltot : 0.f;
+        if constexpr (kRotated) {  // o = H O / (256 L)
+            wave_fwht(y, lane);
+            f *= 1.0f / 256.0f;
+        }
         u32x2 o;
         o.x = static_cast<uint32_t>(f32_to_bf16(y[0] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[1] * f)) << 16);
         o.y = static_cast<uint32_t>(f32_to_bf16(y[2] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[3] * f)) << 16);
         const int i = r / G, h = r - i * G;
         *reinterpret_cast<u32x2 *>(
-            p.out + ((static_cast<int64_t>(b) * a.n_queries + i) * p.n_q + static_cast<int64_t>(g) * G + h) * kDim +
+            a.out + ((static_cast<int64_t>(b) * a.n_queries + i) * a.n_q + static_cast<int64_t>(g) * G + h) * kDim +
             4 * lane) = o;
     }
+}
+
+hipError_t launch_split_combine(const CombineArgs &c, bool rotated, hipStream_t stream) {
+    const dim3 grid(c.rows, c.n_kv, c.batch);
+    if (rotated)
+        hipLaunchKernelGGL(tq4_decode_combine_kernel<true>, grid, dim3(kCombThreads), 0, stream, c);
+    else
+        hipLaunchKernelGGL(tq4_decode_combine_kernel<false>, grid, dim3(kCombThreads), 0, stream, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStream_t stream) {
@@ -652,9 +660,23 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStrea
         default:
             return hipErrorInvalidValue;
     }
-    if (plan.n_splits > 1)
-        hipLaunchKernelGGL(tq4_decode_combine_kernel, dim3(plan.rows, p.n_kv, p.batch), dim3(kCombThreads), 0,
-                           stream, a);
+    if (plan.n_splits > 1) {
+        CombineArgs c;
+        c.parts = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + plan.counters_bytes);
+        c.seq_lens = p.seq_lens;
+        c.out = p.out;
+        c.max_seq_len = p.max_seq_len;
+        c.split_tiles = plan.split_tiles;
+        c.n_splits = plan.n_splits;
+        c.partial_floats = static_cast<int32_t>(plan.partial_floats);
+        c.rows = plan.rows;
+        c.group = plan.group;
+        c.n_queries = plan.n_queries;
+        c.n_q = p.n_q;
+        c.n_kv = p.n_kv;
+        c.batch = p.batch;
+        return launch_split_combine(c, true, stream);
+    }
     return hipGetLastError();
 }
 

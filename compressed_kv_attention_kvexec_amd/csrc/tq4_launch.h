@@ -75,6 +75,76 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStream_t stream);
 
+constexpr int kSplitStatPad = 64;  // floats of each statistic row (M, L) in a split partial
+
+// Merge of split-K partials into bf16 rows (shared by the fused decode and the dense path).  The
+// partial of (request, KV head, split) holds M[rows] and L[rows], each padded to 64 floats, then
+// O[rows][256]; row r is query token r / group, head r % group of the KV head's group.
+struct CombineArgs {
+    const float *parts;      // [batch][n_kv][n_splits][partial_floats]
+    const int32_t *seq_lens;
+    uint16_t *out;           // bf16 [batch][n_queries][n_q][256]
+    int32_t max_seq_len;
+    int32_t split_tiles;     // 32-key tiles per split
+    int32_t n_splits;
+    int32_t partial_floats;
+    int32_t rows;
+    int32_t group;
+    int32_t n_queries;
+    int32_t n_q;
+    int32_t n_kv;
+    int32_t batch;
+};
+// rotated: O is in the rotated domain (the output is H O / (256 L)); else the output is O / L.
+hipError_t launch_split_combine(const CombineArgs &c, bool rotated, hipStream_t stream);
+
+// Unfused path: reconstruction into contiguous bf16 K/V, then dense decode attention.
+struct ReconParams {
+    const uint32_t *k_words;
+    const uint32_t *v_words;
+    const uint16_t *k_norms;
+    const uint16_t *v_norms;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv;
+    const int32_t *page_table;
+    int32_t table_stride;
+    const int32_t *seq_lens;
+    int32_t batch;
+    int32_t max_seq_len;
+    uint16_t *k_out;  // bf16 bits [batch][n_kv][max_seq_len][256]
+    uint16_t *v_out;
+};
+
+hipError_t launch_reconstruct(const ReconParams &p, hipStream_t stream);
+
+struct DensePlan {
+    int32_t group;
+    int32_t waves;        // wavefronts per split workgroup
+    int32_t n_splits;
+    int32_t split_tiles;  // 32-key tiles per workgroup
+    size_t partial_floats;
+    size_t workspace_bytes;
+};
+
+DensePlan plan_dense(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads);
+
+struct DenseParams {
+    const uint16_t *q;  // bf16 bits [batch][n_q][256]
+    const uint16_t *k;  // bf16 bits [batch][n_kv][max_seq_len][256]
+    const uint16_t *v;
+    const int32_t *seq_lens;
+    uint16_t *out;      // bf16 bits [batch][n_q][256]
+    void *workspace;
+    int32_t batch;
+    int32_t max_seq_len;
+    int32_t n_q;
+    int32_t n_kv;
+    float scale;
+};
+
+hipError_t launch_dense(const DenseParams &p, const DensePlan &plan, hipStream_t stream);
+
 struct PrefillPlan {
     int32_t group;
     int32_t q_tokens_per_block;  // chunk tokens per query block

@@ -237,6 +237,60 @@ tq4_status tq4_attn_verify(const tq4_layer_pool *pool, const void *q, tq4_dtype 
                            int32_t n_q_heads, float scale, void *out, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * The unfused path ([KVX]: besides the fused paths, multi-query prefill can
+ * reconstruct pages into contiguous tensors of the query dtype, and gather
+ * plus scaled dot-product attention is the fallback).  It materialises what
+ * the fused entry points never write -- 512 B per vector instead of 130 B --
+ * and exists to measure that cost and to serve callers that need plain K/V.
+ *
+ * tq4_reconstruct_pages -- write each cached position's K and V as bf16:
+ *   k_out, v_out : device bf16 [batch][n_kv_heads][max_seq_len][256], 16-byte
+ *                  aligned.  For request b and position p < L_b (seq_lens[b]
+ *                  clamped to [0, max_seq_len]) the row is n * (H c[idx]) / 16
+ *                  of the record at page page_table[b][p / page_size], offset
+ *                  p % page_size, rounded to bf16 (nearest even).  Positions
+ *                  p >= L_b are not written.  A page ID outside the pool
+ *                  writes zero rows.
+ *   out_dtype    : TQ4_BF16.
+ *   other arguments as for tq4_attn_decode; batch <= 65535.
+ * The transform runs in fp32: each value is within half a bf16 unit of the
+ * exact reconstruction, plus a few fp32 units of the norm for cancellation.
+ */
+tq4_status tq4_reconstruct_pages(const tq4_layer_pool *pool, const int32_t *page_table,
+                                 int32_t page_table_stride, const int32_t *seq_lens, int32_t batch,
+                                 int32_t max_seq_len, tq4_dtype out_dtype, void *k_out, void *v_out,
+                                 void *stream);
+
+/* Bytes of device workspace tq4_sdpa_decode needs (0 for invalid sizes, and 0
+ * when one workgroup covers each request and KV head). */
+size_t tq4_sdpa_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                      int32_t n_kv_heads);
+
+/*
+ * tq4_sdpa_decode -- single-query attention per request over dense K/V:
+ *   q        : device bf16 [batch][n_q_heads][256], 16-byte aligned.
+ *   k, v     : device bf16 [batch][n_kv_heads][max_seq_len][256] (the layout
+ *              tq4_reconstruct_pages writes), 16-byte aligned; rows past each
+ *              request's length are never read.
+ *   q_dtype, kv_dtype : TQ4_BF16.
+ *   seq_lens : device int32 [batch], clamped to [0, max_seq_len]; a request
+ *              with 0 positions gets a zero output.
+ *   n_q_heads: a multiple of n_kv_heads, n_q_heads / n_kv_heads <= 16;
+ *              batch and n_kv_heads <= 65535.
+ *   out      : device bf16 [batch][n_q_heads][256];
+ *              out[b][h] = sum_j softmax_j(scale q.k_j) v_j over KV head
+ *              h / (n_q_heads / n_kv_heads).
+ *   workspace: device, >= tq4_sdpa_decode_workspace_size(...) bytes,
+ *              256-byte aligned (may be NULL when that size is 0); contents on
+ *              entry do not matter; calls sharing it must be ordered on one
+ *              stream.
+ */
+tq4_status tq4_sdpa_decode(const void *q, tq4_dtype q_dtype, const void *k, const void *v,
+                           tq4_dtype kv_dtype, const int32_t *seq_lens, int32_t batch,
+                           int32_t max_seq_len, int32_t n_q_heads, int32_t n_kv_heads, float scale,
+                           void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace tq4_attn_prefill_chunk needs (0 for invalid sizes). */
 size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,
                                        int32_t n_kv_heads, int32_t page_size);

@@ -113,6 +113,35 @@ def test_verify_validation(lib):
     assert _verify(lib, ws_bytes=need - 1) == 5
 
 
+def test_unfused_validation(lib):
+    pool = _pool()
+    rec = lambda **kw: lib.tq4_reconstruct_pages(
+        ctypes.byref(kw.get("pool", pool)), kw.get("table", FAKE), 64, kw.get("seq", FAKE), kw.get("batch", 1),
+        kw.get("max_seq", 4000), kw.get("dtype", B.TQ4_BF16), kw.get("k", FAKE), kw.get("v", FAKE), None)
+    assert rec(pool=_pool(head_dim=64)) == 2
+    assert rec(table=None) == 1
+    assert rec(k=None) == 1
+    assert rec(dtype=B.TQ4_F32) == 3
+    assert rec(batch=0) == 2
+    assert rec(batch=70000) == 2
+    assert rec(max_seq=4097) == 2
+    assert rec(k=FAKE + 8) == 4
+    sd = lambda **kw: lib.tq4_sdpa_decode(
+        kw.get("q", FAKE), B.TQ4_BF16, FAKE, kw.get("v", FAKE), kw.get("kvd", B.TQ4_BF16), FAKE, 1,
+        kw.get("max_seq", 4000), kw.get("n_q", 24), 4, 0.0625, FAKE, kw.get("ws", FAKE), kw.get("ws_bytes", 1 << 30),
+        None)
+    assert sd(q=None) == 1
+    assert sd(kvd=B.TQ4_F32) == 3
+    assert sd(n_q=22) == 2
+    assert sd(n_q=68) == 2
+    assert sd(v=FAKE + 2) == 4
+    assert sd(ws=None) == 5
+    need = lib.tq4_sdpa_decode_workspace_size(1, 4000, 24, 4)
+    assert need > 0 and lib.tq4_sdpa_decode_workspace_size(1, 100, 24, 4) == 0
+    assert sd(ws_bytes=need - 1) == 5
+    assert lib.tq4_sdpa_decode_workspace_size(0, 100, 24, 4) == 0
+
+
 def test_encode_validation(lib):
     pool = _pool()
     enc = lib.tq4_encode_pages
