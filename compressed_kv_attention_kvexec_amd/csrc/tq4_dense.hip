@@ -8,9 +8,9 @@
 // reconstruction writes 512 B per vector that the attention reads back, against 130 B per vector
 // read once by the fused kernels.
 //
-//   tq4_reconstruct_kernel: one wavefront per position (its K and V record), lane l holding dims
-//     4l .. 4l+3: centroid lookup, 256-point Hadamard transform in fp32 (two stages in registers,
-//     six by lane exchange), times norm / 16, bf16 (round to nearest even).
+//   tq4_reconstruct_kernel: one wavefront per run of 16 positions (their K and V records), lane l
+//     holding dims 4l .. 4l+3: centroid lookup, 256-point Hadamard transform in fp32 (two stages
+//     in registers, six by lane exchange), times norm / 16, bf16 (round to nearest even).
 //   tq4_sdpa_split_kernel: split-K decode attention over bf16 K/V [batch][n_kv][max_seq][256].
 //     Per 32-key tile and wavefront: S^T[32 keys][16 heads] = K Q^T with 16 bf16 MFMAs (K rows
 //     are MFMA operands as stored), base-2 online softmax, then O[heads][256] += P V on the vector
@@ -47,11 +47,27 @@ __global__ __launch_bounds__(kRecWaves * kWave) void tq4_reconstruct_kernel(Reco
     __syncthreads();
     const int L_req = p.seq_lens[b];
     const int L = L_req < 0 ? 0 : (L_req > p.max_seq_len ? p.max_seq_len : L_req);
-    const int32_t *pt_row = p.page_table + static_cast<int64_t>(b) * p.table_stride;
-    const int64_t out_row0 = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_seq_len;
+    // this wave's run: kRecPositionsPerWave consecutive positions inside one page (page sizes are
+    // multiples of 32), so one table entry and consecutive records cover it
+    const int pos0 = (blockIdx.x * kRecWaves + wave_u) * kRecPositionsPerWave;
+    if (pos0 >= L) return;
+    const int cnt = min(kRecPositionsPerWave, L - pos0);
+    const int page = p.page_table[static_cast<int64_t>(b) * p.table_stride + pos0 / p.page_size];
+    const bool valid = page >= 0 && page < p.num_pages;  // a page outside the pool reads as zeros
+    const int64_t rec0 = valid ? (static_cast<int64_t>(page) * p.n_kv + g) * p.page_size + pos0 % p.page_size : 0;
+    // every load of the run first: word lane / 2 of each record, and the run's norms one per lane
+    uint32_t kw[kRecPositionsPerWave], vw[kRecPositionsPerWave];
+#pragma unroll
+    for (int j = 0; j < kRecPositionsPerWave; ++j) {
+        const int64_t r = valid ? rec0 + min(j, cnt - 1) : 0;
+        kw[j] = p.k_words[r * kWords + (lane >> 1)];
+        vw[j] = p.v_words[r * kWords + (lane >> 1)];
+    }
+    const int64_t rn = valid ? rec0 + min(lane & (kRecPositionsPerWave - 1), cnt - 1) : 0;
+    const uint32_t nk = p.k_norms[rn], nv = p.v_norms[rn];
     const uint32_t shift = 16u * static_cast<uint32_t>(lane & 1);
-    auto vector_out = [&](const uint32_t *words, uint16_t norm_bits, bool valid, uint16_t *dst) {
-        const uint32_t w = words[lane >> 1];
+    const int64_t o0 = ((static_cast<int64_t>(b) * p.n_kv + g) * p.max_seq_len + pos0) * kDim + 4 * lane;
+    auto vector_out = [&](uint32_t w, uint32_t norm_bits, uint16_t *dst) {
         float y[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) y[j] = cent[(w >> (shift + 4u * j)) & 15u];
@@ -68,22 +84,15 @@ __global__ __launch_bounds__(kRecWaves * kWave) void tq4_reconstruct_kernel(Reco
         enc_stage<8>(y, lane);
         enc_stage<16>(y, lane);
         enc_stage<32>(y, lane);
-        const float f = valid ? f16_bits_to_f32(norm_bits) * (1.0f / 16.0f) : 0.f;  // x = n (H c) / 16
-        u32x2 o;
-        o.x = static_cast<uint32_t>(f32_to_bf16(y[0] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[1] * f)) << 16);
-        o.y = static_cast<uint32_t>(f32_to_bf16(y[2] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[3] * f)) << 16);
-        *reinterpret_cast<u32x2 *>(dst + 4 * lane) = o;
+        const float f = valid ? f16_bits_to_f32(static_cast<uint16_t>(norm_bits)) * (1.0f / 16.0f) : 0.f;  // n (H c) / 16
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(y[0] * f, y[1] * f), pack_bf16x2(y[2] * f, y[3] * f)};
     };
-    const int pos0 = blockIdx.x * (kRecWaves * kRecPositionsPerWave) + wave_u;
+#pragma unroll
     for (int j = 0; j < kRecPositionsPerWave; ++j) {
-        const int pos = pos0 + kRecWaves * j;
-        if (pos >= L) break;  // wave-uniform
-        const int page = pt_row[pos / p.page_size];
-        const bool valid = page >= 0 && page < p.num_pages;  // a page outside the pool reads as zeros
-        const int64_t rec = valid ? (static_cast<int64_t>(page) * p.n_kv + g) * p.page_size + pos % p.page_size : 0;
-        const int64_t o = (out_row0 + pos) * kDim;
-        vector_out(p.k_words + rec * kWords, p.k_norms[rec], valid, p.k_out + o);
-        vector_out(p.v_words + rec * kWords, p.v_norms[rec], valid, p.v_out + o);
+        if (j < cnt) {  // wave-uniform; a guard, not a break, so the loop unrolls
+            vector_out(kw[j], __builtin_amdgcn_readlane(nk, j), p.k_out + o0 + j * kDim);
+            vector_out(vw[j], __builtin_amdgcn_readlane(nv, j), p.v_out + o0 + j * kDim);
+        }
     }
 }
 
@@ -91,6 +100,7 @@ hipError_t launch_reconstruct(const ReconParams &p, hipStream_t stream) {
     ReconArgs a;
     a.p = p;
     for (int i = 0; i < 16; ++i) a.centroid[i] = codebook().centroid[i];
+    static_assert(32 % kRecPositionsPerWave == 0, "a run must stay inside one page");
     const int per_block = kRecWaves * kRecPositionsPerWave;
     const int blocks = (p.max_seq_len + per_block - 1) / per_block;
     hipLaunchKernelGGL(tq4_reconstruct_kernel, dim3(blocks, p.n_kv, p.batch), dim3(kRecWaves * kWave), 0, stream, a);

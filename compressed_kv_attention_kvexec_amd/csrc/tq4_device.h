@@ -30,6 +30,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// Two fp32 -> packed bf16 (a in the low half) with one v_cvt_pk_bf16_f32, round to nearest even:
+// the same bits as f32_to_bf16 for every finite input.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){a, b}, bf16x2_t));
+}
+
 // fp32 -> fp16 bits using the hardware conversion (round to nearest even).
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
     _Float16 h = static_cast<_Float16>(f);
