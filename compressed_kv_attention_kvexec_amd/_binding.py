@@ -18,7 +18,8 @@ HEADER = os.path.join(ROOT, "include", "tq4.h")
 TQ4_OK = 0
 TQ4_F32, TQ4_BF16, TQ4_F16 = 0, 1, 2
 STATUS_NAMES = {0: "TQ4_OK", 1: "TQ4_ERR_NULL", 2: "TQ4_ERR_SHAPE", 3: "TQ4_ERR_DTYPE",
-                4: "TQ4_ERR_ALIGN", 5: "TQ4_ERR_WORKSPACE", 6: "TQ4_ERR_HIP"}
+                4: "TQ4_ERR_ALIGN", 5: "TQ4_ERR_WORKSPACE", 6: "TQ4_ERR_HIP", 7: "TQ4_ERR_CAPACITY"}
+TQ4_ERR_CAPACITY = 7
 
 
 class Tq4Error(RuntimeError):
@@ -77,6 +78,32 @@ def load_library(path: str | None = None):
     lib.tq4_attn_prefill_workspace_size.restype = sz
     lib.tq4_attn_prefill_chunk.argtypes = [pool_p, vp, st, vp, i32, i32, i32, f32, vp, vp, sz, vp]
     lib.tq4_attn_prefill_chunk.restype = st
+    pp = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.tq4_pages_create.argtypes = [i32, i32, ctypes.POINTER(pp)]
+    lib.tq4_pages_create.restype = st
+    lib.tq4_pages_destroy.argtypes = [pp]
+    lib.tq4_pages_destroy.restype = None
+    lib.tq4_pages_admission_need.argtypes = [i64, i64, i32]
+    lib.tq4_pages_admission_need.restype = i64
+    lib.tq4_pages_admit.argtypes = [pp, i64, i64, vp, i32, ctypes.POINTER(i32)]
+    lib.tq4_pages_admit.restype = st
+    lib.tq4_pages_extend.argtypes = [pp, i32, i64]
+    lib.tq4_pages_extend.restype = st
+    lib.tq4_pages_table.argtypes = [pp, i32, vp, i32]
+    lib.tq4_pages_table.restype = i32
+    lib.tq4_pages_finish.argtypes = [pp, i32]
+    lib.tq4_pages_finish.restype = st
+    lib.tq4_pages_boundary.argtypes = [pp]
+    lib.tq4_pages_boundary.restype = st
+    lib.tq4_pages_free_count.argtypes = [pp]
+    lib.tq4_pages_free_count.restype = i32
+    lib.tq4_pages_free_list.argtypes = [pp, vp, i32]
+    lib.tq4_pages_free_list.restype = i32
+    lib.tq4_pages_refcount.argtypes = [pp, i32]
+    lib.tq4_pages_refcount.restype = i32
+    lib.tq4_pages_reserved.argtypes = [pp]
+    lib.tq4_pages_reserved.restype = i64
     _lib = lib
     return lib
 

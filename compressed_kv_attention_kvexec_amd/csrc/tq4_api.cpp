@@ -55,6 +55,7 @@ const char *tq4_status_string(tq4_status status) {
         case TQ4_ERR_ALIGN: return "a pointer is not aligned as required";
         case TQ4_ERR_WORKSPACE: return "workspace missing or too small";
         case TQ4_ERR_HIP: return "HIP runtime error";
+        case TQ4_ERR_CAPACITY: return "not enough free pages or memory";
     }
     return "unknown status";
 }

@@ -87,7 +87,8 @@ typedef enum tq4_status {
     TQ4_ERR_DTYPE = 3,     /* unsupported element type */
     TQ4_ERR_ALIGN = 4,     /* a pointer is not aligned as documented */
     TQ4_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
-    TQ4_ERR_HIP = 6        /* the HIP runtime reported an error */
+    TQ4_ERR_HIP = 6,       /* the HIP runtime reported an error */
+    TQ4_ERR_CAPACITY = 7   /* not enough free pages (or host memory) for the request */
 } tq4_status;
 
 typedef enum tq4_dtype {
@@ -316,6 +317,64 @@ tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4
                                   const int32_t *page_table, int32_t prior_len, int32_t chunk_len,
                                   int32_t n_q_heads, float scale, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * Host page allocator ([ST]: admission reserves page equivalents, shared
+ * prefixes are reference counted, and a departing request gives its pages back
+ * only at the step boundary).  Host memory only, no HIP call; one allocator is
+ * not thread-safe (the caller serialises its calls).  Page IDs index every
+ * layer's pool (tq4_layer_pool) and fill page tables for the attention calls.
+ *
+ * Readings: the free list is first in, first out (pages are handed out from
+ * its head in ID order at creation; returned pages join its tail in the
+ * departing requests' finish order, each request's pages in table order).
+ * Reservations are a budget: a request is admitted while the reservations of
+ * all live requests fit the pool; pages beyond a request's reservation
+ * (output past the guaranteed 8,192 tokens) are taken while free pages remain.
+ */
+typedef struct tq4_page_pool tq4_page_pool;
+
+/* A pool of num_pages pages of page_size positions, all free (IDs 0 ..
+ * num_pages - 1 in order); *out is NULL on error.  Sizes must be >= 1. */
+tq4_status tq4_pages_create(int32_t num_pages, int32_t page_size, tq4_page_pool **out);
+void tq4_pages_destroy(tq4_page_pool *pool);
+
+/* Page equivalents admission reserves: ceil((prompt_len + min(output_budget,
+ * 8192)) / page_size); -1 for negative sizes or page_size < 1. */
+int64_t tq4_pages_admission_need(int64_t prompt_len, int64_t output_budget, int32_t page_size);
+
+/* Admit a request: reserve tq4_pages_admission_need(...) page equivalents if
+ * the live reservations still fit num_pages (else TQ4_ERR_CAPACITY, nothing
+ * changes).  Its page table starts with the n_prefix shared pages (each must be
+ * held by a live request; their reference counts grow by one); they must be
+ * full pages of its prompt (n_prefix * page_size <= prompt_len).  *request_out
+ * receives the request's handle. */
+tq4_status tq4_pages_admit(tq4_page_pool *pool, int64_t prompt_len, int64_t output_budget,
+                           const int32_t *prefix_pages, int32_t n_prefix, int32_t *request_out);
+
+/* Grow a live, not departing request to hold `length` positions: pages are
+ * taken from the free list's head (reference count 1) and appended to its
+ * table.  TQ4_ERR_CAPACITY (nothing changes) if too few pages are free. */
+tq4_status tq4_pages_extend(tq4_page_pool *pool, int32_t request, int64_t length);
+
+/* Copy up to `capacity` of the request's page IDs (position order) into table
+ * (may be NULL); returns the request's page count, -1 for a bad handle. */
+int32_t tq4_pages_table(const tq4_page_pool *pool, int32_t request, int32_t *table, int32_t capacity);
+
+/* Mark a live request as departing: its row leaves at the next boundary. */
+tq4_status tq4_pages_finish(tq4_page_pool *pool, int32_t request);
+
+/* The step boundary: for every departing request, in finish order, drop one
+ * reference on each of its pages in table order (a page reaching zero joins
+ * the free list's tail) and return its reservation; the handle becomes dead. */
+tq4_status tq4_pages_boundary(tq4_page_pool *pool);
+
+/* Observers: free page count; the free list in order (up to capacity entries,
+ * returns its length); a page's reference count; the live reservations. */
+int32_t tq4_pages_free_count(const tq4_page_pool *pool);
+int32_t tq4_pages_free_list(const tq4_page_pool *pool, int32_t *pages, int32_t capacity);
+int32_t tq4_pages_refcount(const tq4_page_pool *pool, int32_t page);
+int64_t tq4_pages_reserved(const tq4_page_pool *pool);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ def test_exports_every_declared_function(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert lib.tq4_abi_version() == 1
-    for st in range(7):
+    for st in range(8):
         assert lib.tq4_status_string(st)
 
 
