@@ -18,6 +18,9 @@ Sources, by page and section:
     dimension 256, 16 full-attention layers, 16,640 B per position vs
     65,536 B in FP16, 3,640 MiB vs 14,336 MiB at 229,376 positions, and
     768 MiB of BF16 K/V for one layer at 192K positions.
+  * same page, section "Reasoning at 200K: 29 of 30 AIME Problems" -- the
+    uniform INT8 KV comparison arm (per-vector symmetric INT8 with an fp16
+    scale, natural domain: the page fixes no format, this is the reading).
 """
 from __future__ import annotations
 
@@ -85,6 +88,15 @@ def _load():
     lib.tq4o_reconstruct.restype = ctypes.c_int
     lib.tq4o_sdpa_dense.argtypes = [c_f64p, c_f64p, c_f64p, i32, i32, i32, i32, c_i32p, ctypes.c_double, c_f64p]
     lib.tq4o_sdpa_dense.restype = ctypes.c_int
+    c_i8p = P(ctypes.c_int8)
+    lib.tq4o_int8_encode_many.argtypes = [c_f32p, i64, c_i8p, c_u16p]
+    lib.tq4o_int8_decode_many.argtypes = [c_i8p, c_u16p, i64, c_f64p]
+    lib.tq4o_int8_encode_to_pool.argtypes = [c_i8p, c_u16p, i32, i32, i32, c_f32p, c_i32p, i32]
+    lib.tq4o_int8_encode_to_pool.restype = ctypes.c_int
+    lib.tq4o_int8_attention.argtypes = [c_i8p, c_u16p, c_i8p, c_u16p, i32, i32, i32,
+                                        c_f64p, i32, i32, c_i32p, i32, c_i32p, c_i32p,
+                                        ctypes.c_double, i32, i32, c_f64p]
+    lib.tq4o_int8_attention.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -363,6 +375,112 @@ def sdpa_dense(q, k, v, seq_lens, scale: float) -> np.ndarray:
     if rc != 0:
         raise MemoryError("oracle sdpa_dense")
     return out
+
+
+# --------------------------------------------------------------------------
+# Uniform INT8 arm ("Fitting a 27B-Parameter LLM into 24 GiB of Laptop Memory",
+# section "Reasoning at 200K: 29 of 30 AIME Problems": a uniform INT8 KV
+# comparison).  Record: 256 signed codes in [-127, 127] and one fp16 scale,
+# natural domain (no rotation); decode is codes * scale.
+# --------------------------------------------------------------------------
+
+def int8_encode(x):
+    """Encode fp32 vectors [..., 256] -> (codes int8 [..., 256], scales fp16 bits [...])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape[-1] == DIM
+    lead = x.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    codes = np.zeros((n, DIM), np.int8)
+    scales = np.zeros((n,), np.uint16)
+    _load().tq4o_int8_encode_many(_ptr(x.reshape(n, DIM), ctypes.c_float), n,
+                                  _ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_uint16))
+    return codes.reshape(*lead, DIM), scales.reshape(lead)
+
+
+def int8_decode(codes, scales) -> np.ndarray:
+    """Exact fp64 values of INT8 records (codes [..., 256], scales [...])."""
+    lead = np.shape(scales)
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    n = int(np.prod(lead)) if lead else 1
+    out = np.zeros((n, DIM), np.float64)
+    _load().tq4o_int8_decode_many(_ptr(codes.reshape(n, DIM), ctypes.c_int8),
+                                  _ptr(scales.reshape(n), ctypes.c_uint16), n, _ptr(out, ctypes.c_double))
+    return out.reshape(*lead, DIM)
+
+
+@dataclass
+class Int8Pool:
+    """One layer's INT8 page pool (host arrays).
+
+    codes: int8 [num_pages][n_kv][P][256]; scales: fp16 bits [num_pages][n_kv][P]."""
+    k_codes: np.ndarray
+    k_scales: np.ndarray
+    v_codes: np.ndarray
+    v_scales: np.ndarray
+
+    @property
+    def num_pages(self):
+        return self.k_codes.shape[0]
+
+    @property
+    def n_kv(self):
+        return self.k_codes.shape[1]
+
+    @property
+    def page_size(self):
+        return self.k_codes.shape[2]
+
+    @staticmethod
+    def empty(num_pages: int, n_kv: int, page_size: int) -> "Int8Pool":
+        shp = (num_pages, n_kv, page_size)
+        return Int8Pool(np.zeros(shp + (DIM,), np.int8), np.zeros(shp, np.uint16),
+                        np.zeros(shp + (DIM,), np.int8), np.zeros(shp, np.uint16))
+
+
+def int8_encode_to_pool(pool: Int8Pool, k_src, v_src, slots) -> None:
+    """Encode source K and V [n_tokens][n_kv][256] (fp32) into INT8 records at slots."""
+    lib = _load()
+    slots = np.ascontiguousarray(slots, dtype=np.int32)
+    for src, codes, scales in ((k_src, pool.k_codes, pool.k_scales), (v_src, pool.v_codes, pool.v_scales)):
+        if src is None:
+            continue
+        src = np.ascontiguousarray(src, dtype=np.float32)
+        assert src.shape == (slots.shape[0], pool.n_kv, DIM)
+        rc = lib.tq4o_int8_encode_to_pool(_ptr(codes, ctypes.c_int8), _ptr(scales, ctypes.c_uint16),
+                                          pool.num_pages, pool.n_kv, pool.page_size,
+                                          _ptr(src, ctypes.c_float), _ptr(slots, ctypes.c_int32), slots.shape[0])
+        if rc != 0:
+            raise ValueError("slot outside the pool")
+
+
+def int8_attn_decode(pool: Int8Pool, q, page_table, seq_lens, scale: float, heads=None) -> np.ndarray:
+    """fp64 single-query decode attention over INT8 pages: q[b] attends positions 0..seq_lens[b]-1
+    of its page-table row.  Returns [batch][n_q][256]; heads outside `heads` stay 0."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    batch, n_q, d = q.shape
+    assert d == DIM and n_q % pool.n_kv == 0
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    if pt.ndim == 1:
+        pt = pt[None, :]
+    rows = np.arange(batch, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    h0, h1 = heads if heads is not None else (0, n_q)
+    out = np.zeros((batch, n_q, DIM), np.float64)
+    rc = _load().tq4o_int8_attention(
+        _ptr(pool.k_codes, ctypes.c_int8), _ptr(pool.k_scales, ctypes.c_uint16),
+        _ptr(pool.v_codes, ctypes.c_int8), _ptr(pool.v_scales, ctypes.c_uint16),
+        pool.num_pages, pool.n_kv, pool.page_size, _ptr(q, ctypes.c_double), n_q, batch,
+        _ptr(pt, ctypes.c_int32), pt.shape[1], _ptr(rows, ctypes.c_int32), _ptr(lens, ctypes.c_int32),
+        float(scale), h0, h1, _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError(f"oracle INT8 attention failed ({rc})")
+    return out
+
+
+def int8_bytes_per_position(n_layers: int = 16, n_kv: int = 4) -> int:
+    """INT8 bytes one cached position occupies across all full-attention layers (K and V)."""
+    return n_layers * n_kv * 2 * (DIM + 2)
 
 
 # --------------------------------------------------------------------------

@@ -489,6 +489,131 @@ int tq4o_sdpa_dense(const double *q, const double *k, const double *v, int32_t b
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Uniform INT8 arm ("Fitting a 27B-Parameter LLM into 24 GiB of Laptop       */
+/* Memory", section "Reasoning at 200K: 29 of 30 AIME Problems": a uniform    */
+/* INT8 KV comparison).  Readings: one symmetric scale per vector, stored as  */
+/* fp16 like the TQ4 norm, codes in [-127, 127], no rotation.                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Encode, fp32 with round-to-nearest-even throughout:
+ *   a = max_d |x_d|;  s16 = fp16(a / 127);  s = (float) s16;
+ *   q_d = clamp(rint(x_d / s), -127, 127), or 0 for every d when s == 0.
+ */
+void tq4o_int8_encode_vec(const float *x, int8_t *codes, uint16_t *scale16) {
+    float a = 0.0f;
+    for (int d = 0; d < TQ4O_DIM; ++d) {
+        const float v = fabsf(x[d]);
+        if (v > a) a = v;
+    }
+    const float s32 = a / 127.0f;
+    const uint16_t s16 = tq4o_f32_to_f16(s32);
+    const float s = (float)tq4o_f16_to_f64(s16);
+    *scale16 = s16;
+    for (int d = 0; d < TQ4O_DIM; ++d) {
+        float q = 0.0f;
+        if (s > 0.0f) {
+            const float r = x[d] / s;
+            q = rintf(r);
+            if (q > 127.0f) q = 127.0f;
+            if (q < -127.0f) q = -127.0f;
+        }
+        codes[d] = (int8_t)q;
+    }
+}
+
+/* Decode: x_d = q_d * s, exact in fp64. */
+void tq4o_int8_decode_vec(const int8_t *codes, uint16_t scale16, double *out) {
+    const double s = tq4o_f16_to_f64(scale16);
+    for (int d = 0; d < TQ4O_DIM; ++d) out[d] = (double)codes[d] * s;
+}
+
+void tq4o_int8_encode_many(const float *x, int64_t n, int8_t *codes, uint16_t *scales) {
+    for (int64_t i = 0; i < n; ++i) tq4o_int8_encode_vec(x + i * TQ4O_DIM, codes + i * TQ4O_DIM, scales + i);
+}
+
+void tq4o_int8_decode_many(const int8_t *codes, const uint16_t *scales, int64_t n, double *out) {
+    for (int64_t i = 0; i < n; ++i) tq4o_int8_decode_vec(codes + i * TQ4O_DIM, scales[i], out + i * TQ4O_DIM);
+}
+
+/* Encode K or V sources [n][n_kv][256] into the INT8 pool at flat slots (page * P + offset). */
+int tq4o_int8_encode_to_pool(int8_t *codes, uint16_t *scales, int32_t num_pages, int32_t n_kv, int32_t P,
+                             const float *src, const int32_t *slots, int32_t n) {
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t slot = slots[i];
+        if (slot < 0 || slot >= num_pages * P) return -1;
+        for (int32_t g = 0; g < n_kv; ++g) {
+            const size_t rec = rec_index(slot / P, g, slot % P, n_kv, P);
+            tq4o_int8_encode_vec(src + ((size_t)i * n_kv + g) * TQ4O_DIM, codes + rec * TQ4O_DIM, scales + rec);
+        }
+    }
+    return 0;
+}
+
+/*
+ * fp64 softmax attention over INT8 pages: the same definition as tq4o_attention with each key and
+ * value taken as its exact INT8 decode (codes times scale, natural domain).
+ */
+int tq4o_int8_attention(const int8_t *k_codes, const uint16_t *k_scales, const int8_t *v_codes,
+                        const uint16_t *v_scales, int32_t num_pages, int32_t n_kv, int32_t P,
+                        const double *q, int32_t n_q, int32_t n_rows, const int32_t *page_table,
+                        int32_t table_stride, const int32_t *row_table, const int32_t *row_len,
+                        double scale, int32_t h_begin, int32_t h_end, double *out) {
+    int32_t group = n_q / n_kv;
+    double kv[TQ4O_DIM];
+    for (int32_t r = 0; r < n_rows; ++r) {
+        int32_t L = row_len[r];
+        const int32_t *table = page_table + (size_t)row_table[r] * table_stride;
+        for (int32_t g = 0; g < n_kv; ++g) {
+            int32_t h0 = g * group, h1 = h0 + group;
+            if (h0 < h_begin) h0 = h_begin;
+            if (h1 > h_end) h1 = h_end;
+            if (h0 >= h1) continue;
+            int32_t nh = h1 - h0;
+            for (int32_t hh = 0; hh < nh; ++hh) {
+                double *oh = out + ((size_t)r * n_q + h0 + hh) * TQ4O_DIM;
+                for (int d = 0; d < TQ4O_DIM; ++d) oh[d] = 0.0;
+            }
+            if (L <= 0) continue;
+            double *s = (double *)malloc((size_t)L * nh * sizeof(double));
+            if (!s) return -2;
+            for (int32_t j = 0; j < L; ++j) {
+                int32_t page = table[j / P];
+                if (page < 0 || page >= num_pages) { free(s); return -1; }
+                size_t rec = rec_index(page, g, j % P, n_kv, P);
+                tq4o_int8_decode_vec(k_codes + rec * TQ4O_DIM, k_scales[rec], kv);
+                for (int32_t hh = 0; hh < nh; ++hh) {
+                    const double *qh = q + ((size_t)r * n_q + h0 + hh) * TQ4O_DIM;
+                    double dot = 0.0;
+                    for (int d = 0; d < TQ4O_DIM; ++d) dot += qh[d] * kv[d];
+                    s[(size_t)hh * L + j] = scale * dot;
+                }
+            }
+            for (int32_t hh = 0; hh < nh; ++hh) {
+                double *sh = s + (size_t)hh * L;
+                double mx = -INFINITY;
+                for (int32_t j = 0; j < L; ++j) if (sh[j] > mx) mx = sh[j];
+                double sum = 0.0;
+                for (int32_t j = 0; j < L; ++j) { sh[j] = exp(sh[j] - mx); sum += sh[j]; }
+                for (int32_t j = 0; j < L; ++j) sh[j] /= sum;
+            }
+            for (int32_t j = 0; j < L; ++j) {
+                int32_t page = table[j / P];
+                size_t rec = rec_index(page, g, j % P, n_kv, P);
+                tq4o_int8_decode_vec(v_codes + rec * TQ4O_DIM, v_scales[rec], kv);
+                for (int32_t hh = 0; hh < nh; ++hh) {
+                    double p = s[(size_t)hh * L + j];
+                    double *oh = out + ((size_t)r * n_q + h0 + hh) * TQ4O_DIM;
+                    for (int d = 0; d < TQ4O_DIM; ++d) oh[d] += p * kv[d];
+                }
+            }
+            free(s);
+        }
+    }
+    return 0;
+}
+
 void tq4o_f64_to_bf16_array(const double *in, uint16_t *out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = tq4o_f64_to_bf16(in[i]);
 }
