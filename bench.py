@@ -275,6 +275,78 @@ def unfused_leg(device, reps: int = 10) -> dict:
             "timing": f"median of {reps} cold calls (768 MiB read before each pair)"}
 
 
+INT8_BYTES_PER_POS_LAYER = 4 * 2 * 258  # 4 KV heads x (K, V) x (256 codes + 2 B scale)
+
+
+def int8_leg(name: str, device, reps: int = 20) -> dict:
+    """The uniform INT8 arm on one layer of a decode workload, timed cold like the TQ4 configs:
+    records written by tq4_int8_encode_pages, one tq4_int8_attn_decode call per timing.  Also
+    times the INT8 encoder over 32,768 tokens."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    import synth
+    w = synth.WORKLOADS[name]
+    table = synth.placement(w, 0)
+    slots = synth.used_slots(w, table)
+    pool = tq4.Int8LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+    sd = torch.from_numpy(slots).to(device)
+    for which, st in ((0, synth.T_K), (1, synth.T_V)):
+        src = synth.torch_normal(synth.seed_of(w.wid, 0, st), (len(slots), w.n_kv, 256), device)
+        for c in range(0, len(slots), 65536):
+            part = src[c:c + 65536]
+            tq4.tq4_int8_encode_pages(pool, part if which == 0 else None, part if which == 1 else None,
+                                      sd[c:c + 65536])
+        del src
+    q = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (w.batch, w.n_q, 256), device).to(torch.bfloat16)
+    tab = torch.from_numpy(table).to(device)
+    seq = torch.tensor(w.seq_lens, dtype=torch.int32, device=device)
+    ws = tq4.new_workspace(tq4.tq4_int8_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv,
+                                                                   w.page_size), device)
+    out = torch.empty_like(q)
+    call = tq4.prepare_int8_decode(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, out, ws)
+    flush = torch.ones(192 << 20, dtype=torch.float32, device=device)
+    for _ in range(3):
+        call()
+    times = []
+    for _ in range(reps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError(f"non-finite INT8 output ({name})")
+    t = sorted(times)[reps // 2]
+    pages = sum(-(-L // w.page_size) for L in w.seq_lens)
+    positions = sum(w.seq_lens)
+    nbytes = positions * INT8_BYTES_PER_POS_LAYER + w.batch * w.n_q * 256 * 2 * 2 + pages * 4 + w.batch * 4
+    # encoder: 32,768 tokens of fp32 K and V
+    tokens = 32768
+    k = synth.torch_normal(synth.seed_of(w.wid, 1, synth.T_K), (tokens, w.n_kv, 256), device)
+    v = synth.torch_normal(synth.seed_of(w.wid, 1, synth.T_V), (tokens, w.n_kv, 256), device)
+    es = sd[:tokens]
+    for _ in range(2):
+        tq4.tq4_int8_encode_pages(pool, k, v, es)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        tq4.tq4_int8_encode_pages(pool, k, v, es)
+    e1.record()
+    torch.cuda.synchronize()
+    te = e0.elapsed_time(e1) / 1e3 / 10
+    enc_bytes = tokens * w.n_kv * 2 * (1024 + 258) + tokens * 4
+    del pool, flush, k, v
+    torch.cuda.empty_cache()
+    return {"workload": name, "cached_positions": list(w.seq_lens), "us_per_call": t * 1e6,
+            "position_layers_per_s": positions / t, "gb_per_s": nbytes / t / 1e9,
+            "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
+            "int8_bytes_per_position_layer": INT8_BYTES_PER_POS_LAYER,
+            "encode_vectors_per_s": tokens * w.n_kv * 2 / te, "encode_gb_per_s": enc_bytes / te / 1e9,
+            "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
+
+
 def prefill_leg(device, reps: int = 3):
     """The chunked-prefill workload: 2,048 bf16 query tokens x 24 heads over 194,560 cached
     positions plus the chunk itself (causal inside the chunk), one layer.  Reports the call
@@ -380,6 +452,8 @@ def main() -> int:
                     help="skip the one-layer cold timings of the packed multi-query verifier")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the reconstruct-then-dense-attention timing")
+    ap.add_argument("--no-int8", action="store_true",
+                    help="skip the uniform INT8 arm timing")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager per-layer launches instead of a HIP graph of the step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -546,6 +620,14 @@ def main() -> int:
         log(f"unfused: reconstruct {r['reconstruct_us']:.1f} us + dense attention {r['sdpa_us']:.1f} us "
             f"= {r['total_us']:.1f} us ({r['unfused_over_fused']:.1f}x the fused call), "
             f"{r['materialized_bf16_kv_bytes'] / 2**20:.0f} MiB of bf16 K/V")
+    if not args.no_int8:
+        r = int8_leg(w.name, dev)
+        tq4_cold = decode_config_leg(w.name, dev)
+        r["tq4_cold_us_per_call"] = tq4_cold["us_per_call"]
+        r["int8_over_tq4"] = r["us_per_call"] / tq4_cold["us_per_call"]
+        result["extra"]["int8"] = r
+        log(f"int8 arm: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s (cold); TQ4 cold "
+            f"{r['tq4_cold_us_per_call']:.1f} us ({r['int8_over_tq4']:.2f}x); encode {r['encode_gb_per_s']:.0f} GB/s")
     if not args.no_prefill:
         log("prefill leg ...")
         result["extra"]["prefill"] = prefill_leg(dev)

@@ -6,6 +6,8 @@ in the library's HIP kernels.
 
 Pool layout (one layer): k_words / v_words int32 bit patterns of uint32 words
 [num_pages][n_kv][page_size][32]; k_norms / v_norms int16 bit patterns of fp16
+[num_pages][n_kv][page_size].  The uniform INT8 arm's pools hold int8 codes
+[num_pages][n_kv][page_size][256] and int16 bit patterns of fp16 scales
 [num_pages][n_kv][page_size].
 """
 from __future__ import annotations
@@ -16,7 +18,7 @@ from dataclasses import dataclass
 import torch
 
 from ._binding import (TQ4_BF16, TQ4_F16, TQ4_F32, Tq4Error, check, header_functions,
-                       load_library, tq4_layer_pool)
+                       load_library, tq4_int8_pool, tq4_layer_pool)
 
 __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_encode_pages",
            "tq4_attn_decode_workspace_size", "tq4_attn_decode", "tq4_attn_prefill_workspace_size",
@@ -24,7 +26,9 @@ __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_e
            "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill",
            "tq4_attn_decode_append", "prepare_decode_append", "tq4_attn_verify_workspace_size",
            "tq4_attn_verify", "prepare_verify", "tq4_reconstruct_pages", "tq4_sdpa_decode_workspace_size",
-           "tq4_sdpa_decode", "prepare_reconstruct", "prepare_sdpa_decode"]
+           "tq4_sdpa_decode", "prepare_reconstruct", "prepare_sdpa_decode", "Int8LayerPool",
+           "tq4_int8_encode_pages", "tq4_int8_attn_decode_workspace_size", "tq4_int8_attn_decode",
+           "prepare_int8_decode"]
 
 HEAD_DIM = 256
 WORDS = 32
@@ -244,6 +248,77 @@ def tq4_attn_prefill_chunk(pool: Tq4LayerPool, q: torch.Tensor, page_table: torc
     return out
 
 
+@dataclass
+class Int8LayerPool:
+    """One layer's pool of uniform INT8 records (codes and fp16 scales)."""
+    k_codes: torch.Tensor
+    v_codes: torch.Tensor
+    k_scales: torch.Tensor
+    v_scales: torch.Tensor
+
+    @staticmethod
+    def empty(num_pages: int, n_kv: int, page_size: int, device="cuda") -> "Int8LayerPool":
+        shp = (num_pages, n_kv, page_size)
+        return Int8LayerPool(torch.zeros(shp + (HEAD_DIM,), dtype=torch.int8, device=device),
+                             torch.zeros(shp + (HEAD_DIM,), dtype=torch.int8, device=device),
+                             torch.zeros(shp, dtype=torch.int16, device=device),
+                             torch.zeros(shp, dtype=torch.int16, device=device))
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_codes.shape[0]
+
+    @property
+    def n_kv(self) -> int:
+        return self.k_codes.shape[1]
+
+    @property
+    def page_size(self) -> int:
+        return self.k_codes.shape[2]
+
+    def struct(self) -> tq4_int8_pool:
+        for t in (self.k_codes, self.v_codes, self.k_scales, self.v_scales):
+            if not t.is_contiguous():
+                raise ValueError("pool tensors must be contiguous")
+        return tq4_int8_pool(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
+                             self.k_scales.data_ptr(), self.v_scales.data_ptr(),
+                             self.num_pages, self.page_size, self.n_kv, HEAD_DIM)
+
+
+def tq4_int8_encode_pages(pool: Int8LayerPool, k, v, slots: torch.Tensor, stream=None) -> None:
+    """Encode [n_tokens][n_kv][256] fp32/bf16 K and/or V into INT8 records at slots (int32)."""
+    src = k if k is not None else v
+    if src is None:
+        raise ValueError("need k or v")
+    for t in (k, v):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("sources must be contiguous")
+    ps = pool.struct()
+    check(load_library().tq4_int8_encode_pages(ctypes.byref(ps), _ptr(k), _ptr(v), _dtype_code(src),
+                                               _ptr(slots), int(slots.shape[0]), _stream(stream)))
+
+
+def tq4_int8_attn_decode_workspace_size(batch: int, max_seq_len: int, n_q_heads: int, n_kv_heads: int,
+                                        page_size: int) -> int:
+    return int(load_library().tq4_int8_attn_decode_workspace_size(batch, max_seq_len, n_q_heads,
+                                                                   n_kv_heads, page_size))
+
+
+def tq4_int8_attn_decode(pool: Int8LayerPool, q: torch.Tensor, page_table: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """q [batch][n_q][256] bf16 over INT8 pages; page_table int32 [batch][stride]; seq_lens int32 [batch]."""
+    batch, n_q, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_int8_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                      pool.page_size), q.device)
+    prepare_int8_decode(pool, q, page_table, seq_lens, max_seq_len, scale, out, workspace, stream)()
+    return out
+
+
 class PreparedCall:
     """A library call with its ctypes arguments marshalled once.
 
@@ -329,3 +404,15 @@ def prepare_decode_append(pool: Tq4LayerPool, k_new, v_new, new_slots: torch.Ten
             _stream(stream))
     return PreparedCall(load_library().tq4_attn_decode_append, args,
                         (ps, pool, k_new, v_new, new_slots, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_int8_decode(pool: Int8LayerPool, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                        max_seq_len: int, scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                        stream=None) -> PreparedCall:
+    batch, n_q, _ = q.shape
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+            _ptr(seq_lens), batch, int(max_seq_len), n_q, ctypes.c_float(scale), _ptr(out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return PreparedCall(load_library().tq4_int8_attn_decode, args,
+                        (ps, pool, q, page_table, seq_lens, out, workspace))

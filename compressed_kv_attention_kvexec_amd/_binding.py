@@ -35,6 +35,13 @@ class tq4_layer_pool(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
 
 
+class tq4_int8_pool(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -78,6 +85,13 @@ def load_library(path: str | None = None):
     lib.tq4_attn_prefill_workspace_size.restype = sz
     lib.tq4_attn_prefill_chunk.argtypes = [pool_p, vp, st, vp, i32, i32, i32, f32, vp, vp, sz, vp]
     lib.tq4_attn_prefill_chunk.restype = st
+    i8p = ctypes.POINTER(tq4_int8_pool)
+    lib.tq4_int8_encode_pages.argtypes = [i8p, vp, vp, st, vp, i32, vp]
+    lib.tq4_int8_encode_pages.restype = st
+    lib.tq4_int8_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.tq4_int8_attn_decode_workspace_size.restype = sz
+    lib.tq4_int8_attn_decode.argtypes = [i8p, vp, st, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
+    lib.tq4_int8_attn_decode.restype = st
     pp = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.tq4_pages_create.argtypes = [i32, i32, ctypes.POINTER(pp)]

@@ -25,6 +25,16 @@ tq4_status check_pool(const tq4_layer_pool *pool) {
     return TQ4_OK;
 }
 
+tq4_status check_int8_pool(const tq4_int8_pool *pool) {
+    if (pool == nullptr) return TQ4_ERR_NULL;
+    if (pool->head_dim != TQ4_HEAD_DIM) return TQ4_ERR_SHAPE;
+    if (pool->page_size < 32 || pool->page_size > 1024 || pool->page_size % 32 != 0) return TQ4_ERR_SHAPE;
+    if (pool->num_pages < 1 || pool->n_kv_heads < 1) return TQ4_ERR_SHAPE;
+    const int64_t recs = int64_t{pool->num_pages} * pool->n_kv_heads * pool->page_size;
+    if (recs > kMaxRecords) return TQ4_ERR_SHAPE;
+    return TQ4_OK;
+}
+
 tq4_status check_pool_reads(const tq4_layer_pool *pool) {
     if (!pool->k_words || !pool->v_words || !pool->k_norms || !pool->v_norms) return TQ4_ERR_NULL;
     if (!aligned(pool->k_words, 16) || !aligned(pool->v_words, 16)) return TQ4_ERR_ALIGN;
@@ -315,6 +325,87 @@ tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4
     p.out = static_cast<uint16_t *>(out);
     p.workspace = workspace;
     return from_hip(tq4::launch_prefill(p, plan, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- uniform INT8 arm
+
+tq4_status tq4_int8_encode_pages(const tq4_int8_pool *pool, const void *k, const void *v,
+                                 tq4_dtype src_dtype, const int32_t *slots, int32_t n_tokens,
+                                 void *stream) {
+    tq4_status st = check_int8_pool(pool);
+    if (st != TQ4_OK) return st;
+    if (k == nullptr && v == nullptr) return TQ4_ERR_NULL;
+    if (n_tokens < 0) return TQ4_ERR_SHAPE;
+    if (src_dtype != TQ4_F32 && src_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
+    if (k != nullptr && (!pool->k_codes || !pool->k_scales)) return TQ4_ERR_NULL;
+    if (v != nullptr && (!pool->v_codes || !pool->v_scales)) return TQ4_ERR_NULL;
+    if (n_tokens > 0 && slots == nullptr) return TQ4_ERR_NULL;
+    if ((k && !aligned(k, 16)) || (v && !aligned(v, 16))) return TQ4_ERR_ALIGN;
+    if ((k && !aligned(pool->k_codes, 16)) || (v && !aligned(pool->v_codes, 16))) return TQ4_ERR_ALIGN;
+    if ((k && !aligned(pool->k_scales, 8)) || (v && !aligned(pool->v_scales, 8))) return TQ4_ERR_ALIGN;
+    if (!aligned(slots, 4)) return TQ4_ERR_ALIGN;
+    if (n_tokens == 0) return TQ4_OK;
+    tq4::Int8EncodeParams p{};
+    p.codes[0] = k ? pool->k_codes : nullptr;
+    p.codes[1] = v ? pool->v_codes : nullptr;
+    p.scales[0] = k ? pool->k_scales : nullptr;
+    p.scales[1] = v ? pool->v_scales : nullptr;
+    p.src[0] = k;
+    p.src[1] = v;
+    p.src_bf16 = src_dtype == TQ4_BF16;
+    p.slots = slots;
+    p.n_tokens = n_tokens;
+    p.n_kv = pool->n_kv_heads;
+    p.page_size = pool->page_size;
+    p.num_slots = pool->num_pages * pool->page_size;
+    return from_hip(tq4::launch_int8_encode(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t tq4_int8_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t page_size) {
+    return tq4_attn_decode_workspace_size(batch, max_seq_len, n_q_heads, n_kv_heads, page_size);
+}
+
+tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype,
+                                const int32_t *page_table, int32_t page_table_stride,
+                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                int32_t n_q_heads, float scale, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    tq4_status st = check_int8_pool(pool);
+    if (st != TQ4_OK) return st;
+    if (!pool->k_codes || !pool->v_codes || !pool->k_scales || !pool->v_scales) return TQ4_ERR_NULL;
+    if (!aligned(pool->k_codes, 16) || !aligned(pool->v_codes, 16)) return TQ4_ERR_ALIGN;
+    if (!aligned(pool->k_scales, 8) || !aligned(pool->v_scales, 8)) return TQ4_ERR_ALIGN;
+    if (!q || !page_table || !seq_lens || !out) return TQ4_ERR_NULL;
+    if (q_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
+    if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
+    if (batch < 1 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return TQ4_ERR_ALIGN;
+    const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads, 1);
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return TQ4_ERR_WORKSPACE;
+    if (workspace != nullptr && !aligned(workspace, 256)) return TQ4_ERR_ALIGN;
+    tq4::Int8DecodeParams p{};
+    p.k_codes = pool->k_codes;
+    p.v_codes = pool->v_codes;
+    p.k_scales = pool->k_scales;
+    p.v_scales = pool->v_scales;
+    p.num_pages = pool->num_pages;
+    p.page_size = pool->page_size;
+    p.n_kv = pool->n_kv_heads;
+    p.q = static_cast<const uint16_t *>(q);
+    p.page_table = page_table;
+    p.table_stride = page_table_stride;
+    p.seq_lens = seq_lens;
+    p.batch = batch;
+    p.max_seq_len = max_seq_len;
+    p.n_q = n_q_heads;
+    p.scale = scale;
+    p.out = static_cast<uint16_t *>(out);
+    p.workspace = workspace;
+    return from_hip(tq4::launch_int8_decode(p, plan, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

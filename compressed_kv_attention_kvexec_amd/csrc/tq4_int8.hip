@@ -1,0 +1,567 @@
+// tq4_int8.hip -- the uniform INT8 KV arm on gfx950: encoder and single-query decode attention over
+// INT8 pages ("Fitting a 27B-Parameter LLM into 24 GiB of Laptop Memory", section "Reasoning at
+// 200K: 29 of 30 AIME Problems": a uniform INT8 KV cache is the comparison arm of the TQ4 run).
+//
+// Record (the page fixes no format; this is the plain per-vector reading): 256 signed codes q_d in
+// [-127, 127] and one fp16 scale s; the vector is q * s in the natural domain (no rotation).
+// Encoding, fp32 with round to nearest even: s = fp16(max_d |x_d| / 127), q_d = clamp(rint(x_d / s),
+// -127, 127), every code 0 when s == 0.
+//
+// Decode attention keeps the work decomposition of the TQ4 decode kernel: grid (split, KV head,
+// request); the G query heads of a KV head are the 16 MFMA columns; the 8 wavefronts of a split
+// take every 8th 32-key tile, two per SIMD.  Per tile and wavefront:
+//   S^T[32 keys][16] = C_K . Q^T       codes -> fp16 exactly     16 x v_mfma_f32_16x16x32_f16
+//   x_j = S_j s_k,j, online softmax in base 2 (lazy rescale as in the TQ4 kernel)
+//   O^T[256][16] += (C_V s_v)^T . P^T  each value code * scale rounded once to fp16, 16 MFMAs
+// A code becomes fp16 with one v_cvt_f16_i16 reading the byte with sign extension (SDWA), so no
+// table and no shift or pack instructions sit between the loads and the MFMAs.  The splits are
+// merged by the shared combine kernel in the natural domain (o = O / L).
+//
+// Lane layout (lane = 16 gq + n):
+//   K: M-tile mt, K-step ks: lane holds key 16 mt + n, dims 64 (ks / 2) + 16 gq + 8 (ks % 2) .. +7,
+//      from one 16-byte load per (mt, ks / 2); the query operand uses the same dims per column n.
+//   scores: lane holds column n, keys sigma(j) = j < 4 ? 4 gq + j : 16 + 4 gq + j - 4.
+//   V: lane loads dims 16 n .. 16 n + 15 of keys sigma(0..7); M-tile e (0..15) takes byte e of
+//      each key, so its row n is dim 16 n + e and lane (gq, n) accumulates dims 16 (4 gq + r) + e.
+#pragma clang fp contract(off)
+
+#include <cfloat>
+
+#include "tq4_device.h"
+#include "tq4_encode_wave.h"
+#include "tq4_launch.h"
+#include "tq4_tile.h"
+
+namespace tq4 {
+
+// ---------------------------------------------------------------- encoder
+
+constexpr int kI8EncWaves = 4;
+constexpr int64_t kI8EncMaxWorkgroups = 2048;
+constexpr int kI8DropOffset = 0x40000000;  // a buffer offset past any record: the store is dropped
+constexpr int kI8BufferFlags = 0x00020000;
+
+struct Int8EncodeArgs {
+    Int8EncodeParams p;
+};
+
+__device__ __forceinline__ float wave_max_abs(const float x[4]) {
+    float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, kWave));
+    return m;
+}
+
+// One code: clamp(rint(x / s), -127, 127) as a byte (s > 0), correctly rounded division.
+__device__ __forceinline__ uint32_t int8_code(float x, float s) {
+    const float q = fminf(fmaxf(__builtin_rintf(x / s), -127.0f), 127.0f);
+    return static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu;
+}
+
+// Each wavefront encodes vectors wave0, wave0 + stride, ... ([half][token][kv head] order); lane l
+// holds dims 4 l .. 4 l + 3 and stores their four codes as one word; lane 0 stores the scale.  The
+// next vector is requested before the current one is encoded; stores go through buffer resources
+// that cover the record exactly, or nothing for a slot outside the pool.
+template <bool BF16>
+__global__ __launch_bounds__(kI8EncWaves * kWave) void tq4_int8_encode_kernel(Int8EncodeArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave0 = static_cast<int>(blockIdx.x) * kI8EncWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int stride = static_cast<int>(gridDim.x) * kI8EncWaves;
+    const int per_half = a.p.n_tokens * a.p.n_kv;
+    const int first_half = a.p.src[0] != nullptr ? 0 : 1;
+    const int total = per_half * ((a.p.src[0] != nullptr) + (a.p.src[1] != nullptr));
+    if (wave0 >= total) return;
+    constexpr size_t esize = BF16 ? 2 : 4;
+    auto half_of = [&](int vec) { return first_half + static_cast<int>(vec >= per_half); };
+    auto rem_of = [&](int vec) { return vec - (vec >= per_half ? per_half : 0); };
+    auto load = [&](int vec, float x[4], int &slot) {
+        const int rem = rem_of(vec);
+        encode_load(static_cast<const char *>(a.p.src[half_of(vec)]) + static_cast<int64_t>(rem) * kDim * esize, BF16,
+                    lane, x);
+        slot = a.p.slots[rem / a.p.n_kv];
+    };
+    const int scale_off = lane == 0 ? 0 : kI8DropOffset;
+    auto encode_store = [&](int vec, const float x[4], int slot, bool live) {
+        const int half = half_of(vec);
+        const int head = rem_of(vec) % a.p.n_kv;
+        const int s_u = __builtin_amdgcn_readfirstlane(slot);
+        const bool valid = live && s_u >= 0 && s_u < a.p.num_slots;
+        const int sl = valid ? s_u : 0;
+        const int page = sl / a.p.page_size;
+        const int64_t rec = (static_cast<int64_t>(page) * a.p.n_kv + head) * a.p.page_size + (sl - page * a.p.page_size);
+        const float amax = wave_max_abs(x);
+        const uint16_t s16 = f32_to_f16_bits(amax / 127.0f);
+        const float s = f16_bits_to_f32(s16);
+        uint32_t word = 0;
+        if (s > 0.0f)
+            word = int8_code(x[0], s) | (int8_code(x[1], s) << 8) | (int8_code(x[2], s) << 16) | (int8_code(x[3], s) << 24);
+        const __amdgpu_buffer_rsrc_t cr =
+            __builtin_amdgcn_make_buffer_rsrc(a.p.codes[half] + rec * kDim, 0, valid ? kDim : 0, kI8BufferFlags);
+        const __amdgpu_buffer_rsrc_t sr =
+            __builtin_amdgcn_make_buffer_rsrc(a.p.scales[half] + rec, 0, valid ? 2 : 0, kI8BufferFlags);
+        __builtin_amdgcn_raw_buffer_store_b32(word, cr, 4 * lane, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(s16, sr, scale_off, 0, 0);
+    };
+    float x0[4], x1[4];
+    int slot0, slot1;
+    load(wave0, x0, slot0);
+    for (int vec = wave0; vec < total; vec += 2 * stride) {
+        const bool live1 = vec < total - stride;
+        const int v1 = live1 ? vec + stride : vec;
+        load(v1, x1, slot1);
+        __builtin_amdgcn_sched_barrier(0);
+        encode_store(vec, x0, slot0, true);
+        const int v2 = vec < total - 2 * stride ? vec + 2 * stride : vec;
+        load(v2, x0, slot0);
+        __builtin_amdgcn_sched_barrier(0);
+        encode_store(v1, x1, slot1, live1);
+    }
+}
+
+hipError_t launch_int8_encode(const Int8EncodeParams &p, hipStream_t stream) {
+    Int8EncodeArgs a;
+    a.p = p;
+    const int halves = (p.src[0] != nullptr) + (p.src[1] != nullptr);
+    const int64_t vectors = static_cast<int64_t>(halves) * p.n_tokens * p.n_kv;
+    if (vectors == 0) return hipSuccess;
+    if (vectors > 0x7fffffff - 2 * kI8EncMaxWorkgroups * kI8EncWaves) return hipErrorInvalidValue;
+    int64_t blocks = (vectors + kI8EncWaves - 1) / kI8EncWaves;
+    if (blocks > kI8EncMaxWorkgroups) blocks = kI8EncMaxWorkgroups;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kI8EncWaves * kWave);
+    if (p.src_bf16)
+        hipLaunchKernelGGL(tq4_int8_encode_kernel<true>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(tq4_int8_encode_kernel<false>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decode attention
+
+constexpr int kI8Waves = 8;
+constexpr float kI8RescaleSlack = 8.0f;  // log2 headroom before the running maximum is moved
+
+struct Int8DecodeArgs {
+    Int8DecodeParams p;
+    int32_t group;
+    int32_t n_splits;
+    int32_t split_tiles;
+    int32_t partial_floats;
+    uint64_t parts_off;  // byte offset of the partials inside the workspace
+};
+
+// Two signed bytes -> packed fp16 (exact): byte SA of a in the low half, byte SB of b in the high
+// half, each by one v_cvt_f16_i16 whose source operand selects the byte and sign-extends it.
+#define TQ4_I8X2_ASM(SA, SB)                                                                       \
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" #SA \
+        "\n\tv_cvt_f16_i16_sdwa %0, sext(%2) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_" #SB \
+        : "=&v"(r)                                                                                 \
+        : "v"(a), "v"(b))
+template <int SA, int SB>
+__device__ __forceinline__ uint32_t i8x2_to_f16x2(uint32_t a, uint32_t b) {
+    uint32_t r;
+    if constexpr (SA == 0 && SB == 1) TQ4_I8X2_ASM(0, 1);
+    else if constexpr (SA == 2 && SB == 3) TQ4_I8X2_ASM(2, 3);
+    else if constexpr (SA == 0 && SB == 0) TQ4_I8X2_ASM(0, 0);
+    else if constexpr (SA == 1 && SB == 1) TQ4_I8X2_ASM(1, 1);
+    else if constexpr (SA == 2 && SB == 2) TQ4_I8X2_ASM(2, 2);
+    else {
+        static_assert(SA == 3 && SB == 3, "byte pair not instantiated");
+        TQ4_I8X2_ASM(3, 3);
+    }
+    return r;
+}
+#undef TQ4_I8X2_ASM
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, a) * __builtin_bit_cast(half2v, b));
+}
+
+// Byte e of keys sigma(0..7) (dims 16 n + e), times their value scales: the A operand of V M-tile e.
+template <int E>
+__device__ __forceinline__ half8 v_operand(const u32x4 v[8], const u32x2 vn[2]) {
+    constexpr int W = E >> 2, C = E & 3;
+    u32x4 r;
+    r.x = mul_f16x2(i8x2_to_f16x2<C, C>(v[0][W], v[1][W]), vn[0].x);
+    r.y = mul_f16x2(i8x2_to_f16x2<C, C>(v[2][W], v[3][W]), vn[0].y);
+    r.z = mul_f16x2(i8x2_to_f16x2<C, C>(v[4][W], v[5][W]), vn[1].x);
+    r.w = mul_f16x2(i8x2_to_f16x2<C, C>(v[6][W], v[7][W]), vn[1].y);
+    return __builtin_bit_cast(half8, r);
+}
+
+template <int E, int ITER_END>
+struct VSteps {
+    __device__ __forceinline__ static void run(const u32x4 v[8], const u32x2 vn[2], half8 pop, float4v oacc[16]) {
+        oacc[E] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v_operand<E>(v, vn), pop, oacc[E], 0, 0, 0);
+        VSteps<E + 1, ITER_END>::run(v, vn, pop, oacc);
+    }
+};
+template <int ITER_END>
+struct VSteps<ITER_END, ITER_END> {
+    __device__ __forceinline__ static void run(const u32x4 *, const u32x2 *, half8, float4v *) {}
+};
+
+struct I8KRegs {
+    u32x4 k[2][4];  // [M-tile][h]: bytes 64 h + 16 gq .. +15 of key 16 mt + n
+    u32x2 kn[2];    // K scales of keys sigma(0..3) and sigma(4..7)
+};
+struct I8VRegs {
+    u32x4 v[8];     // bytes 16 n .. 16 n + 15 of key sigma(j)
+    u32x2 vn[2];    // V scales of the same keys
+};
+
+struct I8LaneOffsets {
+    uint32_t k;    // key n, byte 16 gq
+    uint32_t v;    // key 4 gq, byte 16 n
+    uint32_t nrm;  // scale of key 4 gq
+};
+
+__device__ __forceinline__ I8LaneOffsets i8_lane_offsets(int lane) {
+    const uint32_t n = lane & 15, gq = lane >> 4;
+    return {n * 256u + gq * 16u, gq * 1024u + n * 16u, gq * 8u};
+}
+
+__device__ __forceinline__ void i8_load_k(const Int8DecodeParams &p, int64_t rec0, const I8LaneOffsets &o, I8KRegs &t) {
+    const char *cb = reinterpret_cast<const char *>(p.k_codes) + rec0 * kDim;
+    const char *sb = reinterpret_cast<const char *>(p.k_scales) + rec0 * 2;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) t.k[mt][h] = *reinterpret_cast<const u32x4 *>(cb + o.k + (4096u * mt + 64u * h));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) t.kn[h] = *reinterpret_cast<const u32x2 *>(sb + o.nrm + 32u * h);
+}
+
+__device__ __forceinline__ void i8_load_v(const Int8DecodeParams &p, int64_t rec0, const I8LaneOffsets &o, I8VRegs &t) {
+    const char *cb = reinterpret_cast<const char *>(p.v_codes) + rec0 * kDim;
+    const char *sb = reinterpret_cast<const char *>(p.v_scales) + rec0 * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t koff = (j < 4) ? 256u * j : 4096u + 256u * (j - 4);
+        t.v[j] = *reinterpret_cast<const u32x4 *>(cb + o.v + koff);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) t.vn[h] = *reinterpret_cast<const u32x2 *>(sb + o.nrm + 32u * h);
+}
+
+__global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8DecodeArgs a) {
+    constexpr int NS = kI8Waves;
+    constexpr int NT = NS * kWave;
+    __shared__ __align__(16) half8 qop_sh[8][kWave];  // query operand per K-step and lane
+    __shared__ __align__(16) float4v tree[NS / 2][16][kWave];
+    __shared__ float stat_m[NS][16];
+    __shared__ float stat_l[NS][16];
+    __shared__ float row_f[16];
+    __shared__ float resL[16];
+    __shared__ int32_t progress[NS];
+
+    const Int8DecodeParams &p = a.p;
+    const int G = a.group;
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+
+    const int L_req = p.seq_lens[b];
+    const int slot = __builtin_amdgcn_readfirstlane(wave);
+    const int split_keys = a.split_tiles * kTile;
+    const int key_begin = s * split_keys;
+    const int32_t *pt_row = p.page_table + static_cast<int64_t>(b) * p.table_stride;
+    auto row_off = [&](int h) -> int64_t { return (static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G + h) * kDim; };
+
+    int pid_vec = 0;
+    auto fetch_pids = [&](int chunk) {
+        const int tile = slot + (chunk * kWave + lane) * NS;
+        pid_vec = pt_row[min((key_begin + tile * kTile) / p.page_size, p.table_stride - 1)];
+    };
+    auto pid_of = [&](int j) -> int { return __builtin_amdgcn_readlane(pid_vec, j & (kWave - 1)); };
+
+    const I8LaneOffsets lofs = i8_lane_offsets(lane);
+    const I8LaneOffsets dead_ofs{0u, 0u, 0u};
+    auto rec_of = [&](int t, int inext, bool &valid_d) -> int64_t {
+        const int key0 = __builtin_amdgcn_readfirstlane(key_begin + t * kTile);
+        return tile_rec0(p, g, key0, pid_of(inext), valid_d);
+    };
+    I8KRegs kr;
+    I8VRegs vr;
+    bool valid_t = false;
+    auto issue = [&](int t, int inext, bool live) {
+        const int64_t rec = rec_of(t, inext, valid_t);
+        const int64_t r = live ? rec : 0;
+        const I8LaneOffsets o = live ? lofs : dead_ofs;
+        __builtin_amdgcn_sched_barrier(0);
+        i8_load_k(p, r, o, kr);
+        __builtin_amdgcn_sched_barrier(0);
+        i8_load_v(p, r, o, vr);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // query rows, page IDs and the first tile are requested before the length is known
+    const u32x2 q_raw0 = *reinterpret_cast<const u32x2 *>(p.q + row_off(min(slot, G - 1)) + 4 * lane);
+    const u32x2 q_raw1 = *reinterpret_cast<const u32x2 *>(p.q + row_off(min(slot + NS, G - 1)) + 4 * lane);
+    fetch_pids(0);
+    issue(slot, 0, true);
+
+    const int L = L_req < 0 ? 0 : (L_req > p.max_seq_len ? p.max_seq_len : L_req);
+    const int n_active = (L + split_keys - 1) / split_keys;
+    if (s >= n_active) {
+        if (L == 0 && s == 0)
+            for (int i = tid; i < G * kDim; i += NT) p.out[row_off(i / kDim) + (i % kDim)] = 0;
+        return;
+    }
+    const int key_end = min(key_begin + split_keys, L);
+    const int n_tiles = (key_end - key_begin + kTile - 1) / kTile;
+    const int n_mine = slot < n_tiles ? (n_tiles - slot + NS - 1) / NS : 0;
+
+    // ---- query operand: column r (query head r of the group) is written by wavefront r % 8; a
+    // power-of-two scale puts max |q| in [2^13, 2^14) for the fp16 operand
+    if (tid < NS) progress[tid] = 0;
+    auto put_row = [&](int r, u32x2 raw) {
+        const float y[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                            __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+        const int e = q_exponent(wave_max_abs(y));
+        const float qs = ldexpf(1.0f, e);
+        if (lane == 0) row_f[r] = p.scale * 1.4426950408889634f * ldexpf(1.0f, -e);
+        // dims 4 l .. 4 l + 3: K-step 2 (l / 16) + (l / 2) % 2, lane group (l / 4) % 4, bytes 8 (l % 2)
+        const int ks = 2 * (lane >> 4) + ((lane >> 1) & 1);
+        const int dst_lane = 16 * ((lane >> 2) & 3) + r;
+        u32x2 hv;
+        hv.x = pack_f16x2(y[0] * qs, y[1] * qs);
+        hv.y = pack_f16x2(y[2] * qs, y[3] * qs);
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<char *>(&qop_sh[ks][dst_lane]) + 8 * (lane & 1)) = hv;
+    };
+    auto zero_column = [&](int r) {
+        if (lane < 32) reinterpret_cast<u32x4 *>(&qop_sh[lane & 7][16 * (lane >> 3) + r])[0] = u32x4{0u, 0u, 0u, 0u};
+    };
+    if (slot < G) put_row(slot, q_raw0); else zero_column(slot);
+    if (slot + NS < G) put_row(slot + NS, q_raw1); else zero_column(slot + NS);
+    __syncthreads();
+
+    const float fcol = n < G ? row_f[n] : 1.f;
+    const half8 *qop = &qop_sh[0][lane];
+
+    float4v oacc[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) oacc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // Issue priority of the pair of wavefronts on one SIMD (w and w ^ 4), as in the TQ4 kernel:
+    // the younger takes the higher priority while not ahead of its partner, the older only while
+    // behind.  Tile assignment is static, so results do not depend on timing.
+    const int partner = slot ^ (NS / 2);
+    const bool younger = slot >= NS / 2;
+    auto step = [&](int t, int inext, bool live, int done) {
+        if (lane == 0) progress[slot] = done;
+        const int other = __builtin_amdgcn_readfirstlane(progress[partner]);
+        const int key0 = key_begin + t * kTile;
+        const bool valid = valid_t;
+        float4v sacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const u32x4 kw = kr.k[mt][ks >> 1];
+                const uint32_t w0 = (ks & 1) ? kw.z : kw.x;
+                const uint32_t w1 = (ks & 1) ? kw.w : kw.y;
+                u32x4 c;
+                c.x = i8x2_to_f16x2<0, 1>(w0, w0);
+                c.y = i8x2_to_f16x2<2, 3>(w0, w0);
+                c.z = i8x2_to_f16x2<0, 1>(w1, w1);
+                c.w = i8x2_to_f16x2<2, 3>(w1, w1);
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, c), qop[ks * kWave], sacc[mt], 0, 0, 0);
+            }
+        }
+        float ksc[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            ksc[4 * h + 0] = f16lo(kr.kn[h].x);
+            ksc[4 * h + 1] = f16hi(kr.kn[h].x);
+            ksc[4 * h + 2] = f16lo(kr.kn[h].y);
+            ksc[4 * h + 3] = f16hi(kr.kn[h].y);
+        }
+        float xs[8];
+        const int lim = valid ? (key_end - key0) : 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int koff = 16 * h + 4 * gq + r;
+                xs[4 * h + r] = (koff < lim) ? sacc[h][r] * ksc[4 * h + r] : -INFINITY;
+            }
+        const int64_t rec = rec_of(t + NS, inext, valid_t);
+        const int64_t rec_pf = live ? rec : 0;
+        const I8LaneOffsets ofs_pf = live ? lofs : dead_ofs;
+        __builtin_amdgcn_sched_barrier(0);
+        i8_load_k(p, rec_pf, ofs_pf, kr);
+        __builtin_amdgcn_sched_barrier(0);
+        if (younger ? (done <= other) : (done < other))
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
+        float mx = xs[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, xs[j]);
+        float lo, hi;
+        lane_pair<16>(mx, lo, hi);
+        mx = fmaxf(lo, hi);
+        lane_pair<32>(mx, lo, hi);
+        mx = fmaxf(lo, hi) * fcol;
+        if (__any(mx > m_run + kI8RescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) oacc[tt] *= alpha;
+            m_run = m_new;
+        }
+        const float neg_m = -fmaxf(m_run, -FLT_MAX);
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[j], fcol, neg_m));
+            l_run += pv[j];
+        }
+        u32x4 pr;
+        pr.x = pack_f16x2(pv[0], pv[1]);
+        pr.y = pack_f16x2(pv[2], pv[3]);
+        pr.z = pack_f16x2(pv[4], pv[5]);
+        pr.w = pack_f16x2(pv[6], pv[7]);
+        // value scales of masked keys are zeroed: their records (past the length, or never
+        // written) may hold any bits, and code * scale must be an exact 0 for them
+        u32x2 vn[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k0 = 16 * h + 4 * gq;
+            vn[h].x = vr.vn[h].x & ((k0 < lim ? 0xffffu : 0u) | (k0 + 1 < lim ? 0xffff0000u : 0u));
+            vn[h].y = vr.vn[h].y & ((k0 + 2 < lim ? 0xffffu : 0u) | (k0 + 3 < lim ? 0xffff0000u : 0u));
+        }
+        VSteps<0, 16>::run(vr.v, vn, __builtin_bit_cast(half8, pr), oacc);
+        __builtin_amdgcn_sched_barrier(0);
+        i8_load_v(p, rec_pf, ofs_pf, vr);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    for (int c0 = 0; c0 < n_mine; c0 += kWave) {
+        const int cn = min(kWave, n_mine - c0);
+        const int tc = slot + c0 * NS;
+        if (c0 > 0) {
+            fetch_pids(c0 / kWave);
+            issue(tc, 0, true);
+        }
+        for (int i = 0; i < cn; ++i) step(tc + i * NS, i + 1, i + 1 < cn, c0 + i);
+    }
+    __builtin_amdgcn_s_setprio(0);
+
+    // ---- merge the wavefronts: rescale to the workgroup maximum, then a fixed-order tree in LDS
+    float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+    l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
+    if (gq == 0) {
+        stat_m[slot][n] = m_run;
+        stat_l[slot][n] = l_tot;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[j][n]);
+    {
+        const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) oacc[tt] *= f;
+    }
+    if (tid < 16) {
+        float Ls = 0.f;
+        for (int j = 0; j < NS; ++j) {
+            const float mj = stat_m[j][tid];
+            Ls += (mj == -INFINITY) ? 0.f : stat_l[j][tid] * __builtin_amdgcn_exp2f(mj - M);
+        }
+        resL[tid] = Ls;
+    }
+#pragma unroll
+    for (int half = NS / 2; half >= 1; half >>= 1) {
+        if (slot >= half && slot < 2 * half) {
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) tree[slot - half][tt][lane] = oacc[tt];
+        }
+        __syncthreads();
+        if (slot < half) {
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) oacc[tt] += tree[slot][tt][lane];
+        }
+        __syncthreads();
+    }
+    if (slot != 0 || n >= G) return;
+
+    // lane (gq, n), register r of M-tile e: dim 16 (4 gq + r) + e of column n
+    if (n_active > 1) {
+        const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
+        float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
+                     (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
+        if (gq == 0) {
+            dst[n] = M;
+            dst[kSplitStatPad + n] = resL[n];
+        }
+        float *row = dst + 2 * kSplitStatPad + n * kDim;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float *d = row + 16 * (4 * gq + r);
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                *reinterpret_cast<float4 *>(d + 4 * e4) =
+                    make_float4(oacc[4 * e4][r], oacc[4 * e4 + 1][r], oacc[4 * e4 + 2][r], oacc[4 * e4 + 3][r]);
+        }
+        return;
+    }
+    // single split: o = O / L straight to the output
+    const float Lh = resL[n];
+    const float f = Lh > 0.f ? 1.0f / Lh : 0.f;
+    uint16_t *orow = p.out + row_off(n);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        u32x4 o0, o1;
+        o0.x = pack_bf16x2(oacc[0][r] * f, oacc[1][r] * f);
+        o0.y = pack_bf16x2(oacc[2][r] * f, oacc[3][r] * f);
+        o0.z = pack_bf16x2(oacc[4][r] * f, oacc[5][r] * f);
+        o0.w = pack_bf16x2(oacc[6][r] * f, oacc[7][r] * f);
+        o1.x = pack_bf16x2(oacc[8][r] * f, oacc[9][r] * f);
+        o1.y = pack_bf16x2(oacc[10][r] * f, oacc[11][r] * f);
+        o1.z = pack_bf16x2(oacc[12][r] * f, oacc[13][r] * f);
+        o1.w = pack_bf16x2(oacc[14][r] * f, oacc[15][r] * f);
+        u32x4 *d = reinterpret_cast<u32x4 *>(orow + 16 * (4 * gq + r));
+        d[0] = o0;
+        d[1] = o1;
+    }
+}
+
+hipError_t launch_int8_decode(const Int8DecodeParams &p, const DecodePlan &plan, hipStream_t stream) {
+    if (plan.col_blocks != 1 || plan.n_queries != 1 || plan.slots != kI8Waves) return hipErrorInvalidValue;
+    Int8DecodeArgs a;
+    a.p = p;
+    a.group = plan.group;
+    a.n_splits = plan.n_splits;
+    a.split_tiles = plan.split_tiles;
+    a.partial_floats = static_cast<int32_t>(plan.partial_floats);
+    a.parts_off = plan.counters_bytes;
+    const dim3 grid(plan.n_splits, p.n_kv, p.batch);
+    hipLaunchKernelGGL(tq4_int8_split_kernel, grid, dim3(kI8Waves * kWave), 0, stream, a);
+    if (plan.n_splits > 1) {
+        CombineArgs c;
+        c.parts = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + plan.counters_bytes);
+        c.seq_lens = p.seq_lens;
+        c.out = p.out;
+        c.max_seq_len = p.max_seq_len;
+        c.split_tiles = plan.split_tiles;
+        c.n_splits = plan.n_splits;
+        c.partial_floats = static_cast<int32_t>(plan.partial_floats);
+        c.rows = plan.rows;
+        c.group = plan.group;
+        c.n_queries = 1;
+        c.n_q = p.n_q;
+        c.n_kv = p.n_kv;
+        c.batch = p.batch;
+        return launch_split_combine(c, false, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tq4

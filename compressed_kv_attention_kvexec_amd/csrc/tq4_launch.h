@@ -145,6 +145,44 @@ struct DenseParams {
 
 hipError_t launch_dense(const DenseParams &p, const DensePlan &plan, hipStream_t stream);
 
+// Uniform INT8 arm: records of 256 int8 codes and one fp16 scale, pools laid out like the TQ4 pools.
+struct Int8EncodeParams {
+    int8_t *codes[2];  // K, V (NULL: skip that half)
+    uint16_t *scales[2];
+    const void *src[2];
+    int src_bf16;
+    const int32_t *slots;
+    int32_t n_tokens;
+    int32_t n_kv;
+    int32_t page_size;
+    int32_t num_slots;
+};
+
+hipError_t launch_int8_encode(const Int8EncodeParams &p, hipStream_t stream);
+
+struct Int8DecodeParams {
+    const int8_t *k_codes;  // [num_pages][n_kv][page_size][256]
+    const int8_t *v_codes;
+    const uint16_t *k_scales;  // fp16 bits [num_pages][n_kv][page_size]
+    const uint16_t *v_scales;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv;
+    const uint16_t *q;  // bf16 bits [batch][n_q][256]
+    const int32_t *page_table;
+    int32_t table_stride;
+    const int32_t *seq_lens;
+    int32_t batch;
+    int32_t max_seq_len;
+    int32_t n_q;
+    float scale;
+    uint16_t *out;  // bf16 bits [batch][n_q][256]
+    void *workspace;
+};
+
+// plan: plan_decode(batch, max_seq_len, n_q, n_kv, 1)
+hipError_t launch_int8_decode(const Int8DecodeParams &p, const DecodePlan &plan, hipStream_t stream);
+
 struct PrefillPlan {
     int32_t group;
     int32_t q_tokens_per_block;  // chunk tokens per query block

@@ -21,6 +21,8 @@
  *   [ST]  same page, section "StateTrans: Request Transitions at Safe
  *         Boundaries": 256-token pages, page IDs shared between requests with
  *         a common prefix.
+ *   [AIME] same page, section "Reasoning at 200K: 29 of 30 AIME Problems":
+ *         a uniform INT8 KV cache as the comparison arm.
  *   [P5]  "JustFit: Run Qwen 27B Fast with its full 256K context on a 24 GB
  *         Mac" (wpnews.pro), mechanism table, KVExec row: bounded
  *         reconstruction and attention in the rotated domain.
@@ -317,6 +319,57 @@ tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4
                                   const int32_t *page_table, int32_t prior_len, int32_t chunk_len,
                                   int32_t n_q_heads, float scale, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * Uniform INT8 arm ([AIME]: a uniform INT8 KV cache is the comparison arm of
+ * the TQ4 run).  The page gives no format;
+ * the library's reading is one symmetric scale per vector:
+ *   record  : 256 int8 codes q_d in [-127, 127] and one fp16 scale s; the
+ *             vector is q * s (natural domain, no rotation);
+ *   encoding: fp32, round to nearest even: s = fp16(max_d |x_d| / 127) (the
+ *             division correctly rounded), q_d = clamp(rint(x_d / s), -127, 127);
+ *             all codes 0 when s == 0.  Inputs must be finite.
+ * Pool layout, like the TQ4 pools:
+ *   k_codes, v_codes   : int8 [num_pages][n_kv_heads][page_size][256],
+ *                        16-byte aligned
+ *   k_scales, v_scales : fp16 bits [num_pages][n_kv_heads][page_size],
+ *                        8-byte aligned
+ * Limits as for tq4_layer_pool.  Positions, slots and page tables follow the
+ * TQ4 conventions above.
+ */
+typedef struct tq4_int8_pool {
+    int8_t *k_codes;
+    int8_t *v_codes;
+    uint16_t *k_scales;
+    uint16_t *v_scales;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+} tq4_int8_pool;
+
+/* tq4_int8_encode_pages -- write INT8 records for n_tokens new positions;
+ * arguments and slot rules as tq4_encode_pages.  Bit-identical to the
+ * encoding rule above. */
+tq4_status tq4_int8_encode_pages(const tq4_int8_pool *pool, const void *k, const void *v,
+                                 tq4_dtype src_dtype, const int32_t *slots, int32_t n_tokens,
+                                 void *stream);
+
+/* Workspace bytes tq4_int8_attn_decode needs (0 for invalid sizes or when one
+ * workgroup covers each request and KV head). */
+size_t tq4_int8_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t page_size);
+
+/* tq4_int8_attn_decode -- single-query attention over INT8 pages:
+ * out[b][h] = sum_j softmax_j(scale q.k_j) v_j with k_j, v_j the records'
+ * values (codes times scale).  Arguments, limits, clamping, zero output for an
+ * empty request, page-ID masking and workspace rules as tq4_attn_decode.
+ * Records past a request's length may hold any bits. */
+tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype,
+                                const int32_t *page_table, int32_t page_table_stride,
+                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                int32_t n_q_heads, float scale, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Host page allocator ([ST]: admission reserves page equivalents, shared

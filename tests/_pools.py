@@ -57,3 +57,29 @@ def parity(gpu_out, ref: np.ndarray, what: str = ""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert max_abs <= MAX_ABS and rel <= REL_L2, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
     return max_abs, rel
+
+
+def oracle_int8_pool(workload: synth.Workload, layer: int = 0, table=None, fill=None):
+    """INT8 records of the workload's cached positions, encoded by the oracle.  fill: an optional
+    numpy Generator that first fills every record with random bytes (unwritten records then hold
+    arbitrary bits, NaN and infinite scales included)."""
+    table = synth.placement(workload, layer) if table is None else table
+    pool = oracle.Int8Pool.empty(workload.pool_pages, workload.n_kv, workload.page_size)
+    if fill is not None:
+        for a in (pool.k_codes, pool.v_codes):
+            a[...] = fill.integers(-128, 128, a.shape, dtype=np.int8)
+        for a in (pool.k_scales, pool.v_scales):
+            a[...] = fill.integers(0, 1 << 16, a.shape, dtype=np.uint16)
+    slots = synth.used_slots(workload, table)
+    k = synth.kv_source(workload, layer, len(slots), synth.T_K)
+    v = synth.kv_source(workload, layer, len(slots), synth.T_V)
+    oracle.int8_encode_to_pool(pool, k, v, slots)
+    return pool, table
+
+
+def int8_to_device(pool: "oracle.Int8Pool", device="cuda"):
+    import torch
+    from compressed_kv_attention_kvexec_amd import Int8LayerPool
+    cv = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+    return Int8LayerPool(cv(pool.k_codes, np.int8), cv(pool.v_codes, np.int8),
+                         cv(pool.k_scales, np.int16), cv(pool.v_scales, np.int16))

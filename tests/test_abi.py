@@ -177,3 +177,51 @@ def test_prefill_validation(lib):
     assert call(pool=_pool(page_size=40)) == 2
     assert lib.tq4_attn_prefill_workspace_size(100, 0, 24, 4, 256) == 0
     assert lib.tq4_attn_prefill_workspace_size(100, 16, 24, 4, 256) > 0
+
+
+def _i8pool(num_pages=8, page_size=64, n_kv=4, head_dim=256, ptr=FAKE):
+    return B.tq4_int8_pool(ptr, ptr + 0x100000, ptr + 0x200000, ptr + 0x300000,
+                           num_pages, page_size, n_kv, head_dim)
+
+
+def _i8decode(lib, pool=None, q=FAKE, q_dtype=B.TQ4_BF16, table=FAKE, stride=64, seq=FAKE, batch=1,
+              max_seq=4000, n_q=24, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    pool = _i8pool() if pool is None else pool
+    return lib.tq4_int8_attn_decode(ctypes.byref(pool), q, q_dtype, table, stride, seq, batch, max_seq,
+                                    n_q, 0.0625, out, ws, ws_bytes, None)
+
+
+def test_int8_decode_validation(lib):
+    assert lib.tq4_int8_attn_decode(None, FAKE, 1, FAKE, 4, FAKE, 1, 200, 24, 0.0625, FAKE, FAKE, 1 << 30,
+                                    None) == 1
+    assert _i8decode(lib, pool=_i8pool(head_dim=128)) == 2
+    assert _i8decode(lib, pool=_i8pool(page_size=48)) == 2
+    assert _i8decode(lib, pool=_i8pool(num_pages=0)) == 2
+    assert _i8decode(lib, pool=_i8pool(ptr=0)) == 1
+    assert _i8decode(lib, pool=_i8pool(ptr=FAKE + 8)) == 4   # codes need 16-byte alignment
+    assert _i8decode(lib, q=None) == 1
+    assert _i8decode(lib, seq=None) == 1
+    assert _i8decode(lib, q_dtype=B.TQ4_F32) == 3
+    assert _i8decode(lib, n_q=22) == 2
+    assert _i8decode(lib, n_q=68) == 2
+    assert _i8decode(lib, max_seq=4097) == 2
+    assert _i8decode(lib, q=FAKE + 2) == 4
+    assert _i8decode(lib, ws=None) == 5
+    need = lib.tq4_int8_attn_decode_workspace_size(1, 4000, 24, 4, 64)
+    assert need == lib.tq4_attn_decode_workspace_size(1, 4000, 24, 4, 64) > 0
+    assert _i8decode(lib, ws_bytes=need - 1) == 5
+    assert _i8decode(lib, ws=FAKE + 128) == 4
+
+
+def test_int8_encode_validation(lib):
+    enc = lib.tq4_int8_encode_pages
+    p = _i8pool()
+    assert enc(None, FAKE, FAKE, B.TQ4_F32, FAKE, 4, None) == 1
+    assert enc(ctypes.byref(p), None, None, B.TQ4_F32, FAKE, 4, None) == 1
+    assert enc(ctypes.byref(p), FAKE, FAKE, B.TQ4_F16, FAKE, 4, None) == 3
+    assert enc(ctypes.byref(p), FAKE, FAKE, B.TQ4_F32, FAKE, -1, None) == 2
+    assert enc(ctypes.byref(p), FAKE, FAKE, B.TQ4_F32, None, 4, None) == 1
+    assert enc(ctypes.byref(p), FAKE + 4, FAKE, B.TQ4_F32, FAKE, 4, None) == 4
+    assert enc(ctypes.byref(p), FAKE, FAKE, B.TQ4_F32, FAKE + 2, 4, None) == 4
+    assert enc(ctypes.byref(_i8pool(page_size=40)), FAKE, FAKE, B.TQ4_F32, FAKE, 4, None) == 2
+    assert enc(ctypes.byref(p), FAKE, FAKE, B.TQ4_F32, FAKE, 0, None) == 0  # nothing to do

@@ -1,0 +1,176 @@
+"""GPU parity of the uniform INT8 arm: tq4_int8_encode_pages bit-exact against the oracle's
+encoder (fp32 and bf16 sources, ties, tiny and zero vectors, skipped slots), and
+tq4_int8_attn_decode against the oracle's fp64 attention over the same records (max |err| <= 2e-2,
+rel-L2 <= 5e-3), including records past the lengths that hold arbitrary bits and the full
+212,992-position launch on a sampled head."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _pools import bf16_queries, int8_to_device, oracle_int8_pool, parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _encode_gpu(x, slots, num_pages, n_kv, page, bf16=False, which="kv"):
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    dpool = tq4.Int8LayerPool.empty(num_pages, n_kv, page)
+    for t in (dpool.k_codes, dpool.v_codes):
+        t.fill_(0x55)
+    for t in (dpool.k_scales, dpool.v_scales):
+        t.fill_(0x1234)
+    src = torch.from_numpy(x).cuda()
+    if bf16:
+        src = src.to(torch.bfloat16)
+    k = src if "k" in which else None
+    v = (src.flip(0).contiguous() if "k" in which else src) if "v" in which else None
+    tq4.tq4_int8_encode_pages(dpool, k, v, torch.from_numpy(np.asarray(slots, np.int32)).cuda())
+    torch.cuda.synchronize()
+    return dpool
+
+
+def _host(dpool):
+    return (dpool.k_codes.cpu().numpy(), dpool.k_scales.cpu().numpy().view(np.uint16),
+            dpool.v_codes.cpu().numpy(), dpool.v_scales.cpu().numpy().view(np.uint16))
+
+
+def _mixed_sources(rng, n, n_kv):
+    x = rng.standard_normal((n, n_kv, 256)).astype(np.float32)
+    x[0] = 0.0                                                        # zero vectors
+    x[1] *= np.float32(2.0 ** -20)                                    # subnormal fp16 scales
+    x[2] = (rng.integers(-126, 126, (n_kv, 256)) + 0.5).astype(np.float32)  # exact ties at scale 1
+    x[2, :, 0] = 127.0
+    x[3] *= np.float32(3000.0)
+    x[4] = rng.laplace(size=(n_kv, 256)).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_encode_bit_exact(bf16):
+    import torch
+    rng = np.random.default_rng(130)
+    n, n_kv, P, pages = 300, 4, 64, 8
+    x = _mixed_sources(rng, n, n_kv)
+    if bf16:
+        x = synth.bf16_round(x)
+    slots = rng.permutation(pages * P)[:n].astype(np.int32)
+    slots[7] = -1                 # skipped
+    slots[9] = pages * P + 3      # outside the pool: skipped
+    dpool = _encode_gpu(x, slots, pages, n_kv, P, bf16=bf16)
+    kc, ks, vc, vs = _host(dpool)
+    ref = oracle.Int8Pool.empty(pages, n_kv, P)
+    ref.k_codes[...] = 0x55
+    ref.v_codes[...] = 0x55
+    ref.k_scales[...] = 0x1234
+    ref.v_scales[...] = 0x1234
+    keep = (slots >= 0) & (slots < pages * P)
+    oracle.int8_encode_to_pool(ref, x[keep], np.ascontiguousarray(x[::-1][keep]), slots[keep])
+    np.testing.assert_array_equal(kc, ref.k_codes)
+    np.testing.assert_array_equal(ks, ref.k_scales)
+    np.testing.assert_array_equal(vc, ref.v_codes)
+    np.testing.assert_array_equal(vs, ref.v_scales)
+
+
+def test_encode_one_half_only():
+    rng = np.random.default_rng(131)
+    x = _mixed_sources(rng, 40, 2)
+    slots = np.arange(40, dtype=np.int32) * 3
+    for which in ("k", "v"):
+        kc, ks, vc, vs = _host(_encode_gpu(x, slots, 4, 2, 32, which=which))
+        codes, scales = oracle.int8_encode(x)
+        got_c, got_s, other_c, other_s = (kc, ks, vc, vs) if which == "k" else (vc, vs, kc, ks)
+        pg, off = slots // 32, slots % 32
+        np.testing.assert_array_equal(got_c[pg, :, off], codes)
+        np.testing.assert_array_equal(got_s[pg, :, off], scales)
+        assert np.all(other_c == 0x55) and np.all(other_s == 0x1234)
+
+
+def _decode(dpool, q_t, table, lens, max_seq, scale=synth.SCALE, workspace=None):
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    out = tq4.tq4_int8_attn_decode(dpool, q_t.cuda(), torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda(),
+                                   torch.tensor(lens, dtype=torch.int32).cuda(), max_seq, scale, workspace=workspace)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("page,lens,n_q,n_kv", [
+    (64, (3000, 700, 5), 24, 4),      # several splits, ragged tails
+    (256, (5000,), 24, 4),
+    (32, (200, 1, 0, 33), 24, 4),     # one split, a single key, an empty request
+    (64, (2500, 900), 64, 4),         # group of 16
+    (64, (1800,), 4, 4),              # group of 1
+    (128, (4100, 4099), 16, 2),
+])
+def test_decode_matches_oracle(page, lens, n_q, n_kv):
+    w = synth.Workload(140, "i8", "decode", 1, page, sum((L + page - 1) // page for L in lens) + 4,
+                       seq_lens=lens, n_q=n_q, n_kv=n_kv)
+    pool, table = oracle_int8_pool(w)
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    ref = oracle.int8_attn_decode(pool, q64, table, w.seq_lens, synth.SCALE)
+    got = _decode(int8_to_device(pool), q_t, table, w.seq_lens, max(max(lens), 1))
+    parity(got, ref, f"int8 page={page} lens={lens} G={n_q // n_kv}")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[b].float().numpy() == 0.0)
+
+
+def test_decode_ignores_garbage_past_the_lengths():
+    """Unwritten records (random bytes, NaN and infinite scales among them) inside the last tile
+    and past the lengths must not reach the output."""
+    w = synth.Workload(141, "i8g", "decode", 1, 64, 60, seq_lens=(1000, 37, 64 * 5 + 1))
+    pool, table = oracle_int8_pool(w, fill=np.random.default_rng(5))
+    nan_scales = np.isnan(oracle.f16_bits_to_f64(pool.v_scales)).sum()
+    assert nan_scales > 0
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    ref = oracle.int8_attn_decode(pool, q64, table, w.seq_lens, synth.SCALE)
+    got = _decode(int8_to_device(pool), q_t, table, w.seq_lens, 1000)
+    parity(got, ref, "int8 garbage tail")
+
+
+def test_decode_peaked_and_deterministic():
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    w = synth.Workload(142, "i8p", "decode", 1, 64, 140, seq_lens=(6000, 2222))
+    pool, table = oracle_int8_pool(w)
+    q_t, q64 = bf16_queries(w, 0, w.batch, scale=8.0)
+    ref = oracle.int8_attn_decode(pool, q64, table, w.seq_lens, synth.SCALE)
+    dpool = int8_to_device(pool)
+    ws = tq4.new_workspace(tq4.tq4_int8_attn_decode_workspace_size(2, 6000, 24, 4, 64))
+    a = _decode(dpool, q_t, table, w.seq_lens, 6000, workspace=ws)
+    b = _decode(dpool, q_t, table, w.seq_lens, 6000, workspace=ws)
+    assert torch.equal(a, b)
+    parity(a, ref, "int8 peaked")
+
+
+def test_decode_full_212k_sampled_head():
+    """212,992 cached positions in the full launch; the oracle checks one KV head's rows."""
+    name, g, layer = "decode_212k_16l", 2, 3
+    w = synth.WORKLOADS[name]
+    pool, table = oracle_int8_pool(w, layer)
+    q_t, q64 = bf16_queries(w, layer, w.batch)
+    G = w.n_q // w.n_kv
+    ref = oracle.int8_attn_decode(pool, q64, table, w.seq_lens, synth.SCALE, heads=(g * G, (g + 1) * G))
+    got = _decode(int8_to_device(pool), q_t, table, w.seq_lens, max(w.seq_lens))
+    parity(got[:, g * G:(g + 1) * G], ref[:, g * G:(g + 1) * G], "int8 212k")
+
+
+def test_encode_then_decode_round_trip():
+    """GPU-encoded pools give the same attention as oracle-encoded ones (the records are equal)."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    w = synth.Workload(143, "i8rt", "decode", 1, 64, 40, seq_lens=(1500, 400))
+    table = synth.placement(w, 0)
+    slots = synth.used_slots(w, table)
+    k = synth.kv_source(w, 0, len(slots), synth.T_K)
+    v = synth.kv_source(w, 0, len(slots), synth.T_V)
+    dpool = tq4.Int8LayerPool.empty(w.pool_pages, w.n_kv, w.page_size)
+    tq4.tq4_int8_encode_pages(dpool, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                              torch.from_numpy(slots).cuda())
+    pool, _ = oracle_int8_pool(w, 0, table)
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    got = _decode(dpool, q_t, table, w.seq_lens, 1500)
+    ref = oracle.int8_attn_decode(pool, q64, table, w.seq_lens, synth.SCALE)
+    parity(got, ref, "int8 gpu-encoded")
