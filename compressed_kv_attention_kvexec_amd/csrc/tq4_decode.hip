@@ -335,6 +335,10 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
             nv[4 * h + 2] = f16lo(vr.vn[h].y);
             nv[4 * h + 3] = f16hi(vr.vn[h].y);
         }
+        // a masked key's record (past the length, or never written) may hold any bits: its norm
+        // is dropped here, since exp2(-inf) * NaN would not be 0
+#pragma unroll
+        for (int j = 0; j < 8; ++j) nv[j] = ((j < 4 ? 4 * gq + j : 12 + 4 * gq + j) < lim) ? nv[j] : 0.f;
         float mx = xs[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, xs[j]);

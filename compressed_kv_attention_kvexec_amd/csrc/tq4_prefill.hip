@@ -321,7 +321,9 @@ void tq4_prefill_kernel(PrefillArgs a) {
             for (int q = 0; q < 8; ++q) {
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[q], fcol[j], neg_m));
                 l_run[j] += e;
-                pv[q] = e * nv[q];
+                // masked keys past the cached length may hold any bits, NaN norms included
+                const int koff = (q < 4) ? (4 * gq + q) : (16 + 4 * gq + (q - 4));
+                pv[q] = (koff < lim) ? e * nv[q] : 0.f;
             }
             u32x4 pr;
             pr.x = pack_f16x2(pv[0], pv[1]);

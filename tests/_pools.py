@@ -11,10 +11,17 @@ MAX_ABS = 2e-2      # max |gpu - oracle| over an output tensor
 REL_L2 = 5e-3       # ||gpu - oracle||_2 / ||oracle||_2
 
 
-def oracle_pool(workload: synth.Workload, layer: int = 0, heads=None, table=None):
-    """Encode the workload's cached positions with the oracle (heads: KV heads to fill)."""
+def oracle_pool(workload: synth.Workload, layer: int = 0, heads=None, table=None, fill=None):
+    """Encode the workload's cached positions with the oracle (heads: KV heads to fill).  fill: an
+    optional numpy Generator that first fills every record with random bits (unwritten records
+    then hold arbitrary words and norms, NaN and infinity among them)."""
     table = synth.placement(workload, layer) if table is None else table
     pool = oracle.Pool.empty(workload.pool_pages, workload.n_kv, workload.page_size)
+    if fill is not None:
+        for a in (pool.k_words, pool.v_words):
+            a[...] = fill.integers(0, 1 << 32, a.shape, dtype=np.uint32)
+        for a in (pool.k_norms, pool.v_norms):
+            a[...] = fill.integers(0, 1 << 16, a.shape, dtype=np.uint16)
     slots = synth.used_slots(workload, table)
     k = synth.kv_source(workload, layer, len(slots), synth.T_K)
     v = synth.kv_source(workload, layer, len(slots), synth.T_V)

@@ -202,3 +202,15 @@ def test_decode_workspace_reuse_across_pools():
                                   workspace=ws)
         torch.cuda.synchronize()
         parity(got.cpu(), oracle.attn_decode(pool, q64, table, lens, synth.SCALE), f"reuse {lens}")
+
+
+def test_decode_ignores_garbage_past_the_lengths():
+    """Records past the lengths (inside the last tile and beyond) hold random bits, NaN and
+    infinite norms among them; they must not reach the output."""
+    w = synth.Workload(150, "garbage", "decode", 1, 64, 60, seq_lens=(1000, 37, 64 * 5 + 1))
+    pool, table = oracle_pool(w, fill=np.random.default_rng(6))
+    assert np.isnan(oracle.f16_bits_to_f64(pool.v_norms)).any()
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    ref = oracle.attn_decode(pool, q64, table, w.seq_lens, synth.SCALE)
+    got = _run(to_device(pool), q_t, table, w.seq_lens, 1000)
+    parity(got, ref, "garbage tail")

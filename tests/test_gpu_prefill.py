@@ -77,3 +77,15 @@ def test_prefill_full_size_sampled_rows():
     ref = oracle.attn_prefill_rows(pool, q64[rows], rows, table[0], w.prior_len, synth.SCALE,
                                    heads=(g * G, (g + 1) * G))
     parity(got[rows, g * G:(g + 1) * G], ref[:, g * G:(g + 1) * G], "prefill full size")
+
+
+@pytest.mark.parametrize("prior,chunk", [(100, 28), (640, 33)])
+def test_prefill_ignores_garbage_past_the_chunk(prior, chunk):
+    """Records past prior + chunk in the last page hold random bits (NaN norms among them)."""
+    w = synth.Workload(152, "pfgarbage", "prefill", 1, 64, (prior + chunk) // 64 + 5, prior_len=prior,
+                       chunk_len=chunk)
+    pool, table = oracle_pool(w, fill=np.random.default_rng(8))
+    q_t, q64 = bf16_queries(w, 0, chunk)
+    ref = oracle.attn_prefill_rows(pool, q64, np.arange(chunk), table[0], prior, synth.SCALE)
+    got = _prefill(to_device(pool), q_t, table[0], prior)
+    parity(got, ref, f"prefill garbage prior={prior} chunk={chunk}")

@@ -135,3 +135,12 @@ def test_verify_full_212k_sampled_head(k):
     ref = oracle.attn_verify(pool, q64, table, w.seq_lens, synth.SCALE, heads=(g * G, (g + 1) * G))
     got = _verify(to_device(pool), q_t, table, w.seq_lens, max(w.seq_lens))
     parity(got[:, :, g * G:(g + 1) * G], ref[:, :, g * G:(g + 1) * G], f"212k verify k={k}")
+
+
+def test_verify_ignores_garbage_past_the_lengths():
+    w = synth.Workload(151, "vgarbage", "decode", 1, 64, 60, seq_lens=(1000, 37, 64 * 5 + 1))
+    pool, table = oracle_pool(w, fill=np.random.default_rng(7))
+    q_t, q64 = _queries(w, 4)
+    ref = oracle.attn_verify(pool, q64, table, w.seq_lens, synth.SCALE)
+    got = _verify(to_device(pool), q_t, table, w.seq_lens, 1000)
+    parity(got, ref, "verify garbage tail")
