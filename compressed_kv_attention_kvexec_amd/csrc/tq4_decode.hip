@@ -447,13 +447,14 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
         const bool mine = blk >= b0 && blk < b0 + kTreeBlocks;
 #pragma unroll
         for (int half = NS / 2; half >= 1; half >>= 1) {
-            if (mine && slot >= half && slot < 2 * half) {
+            // only lanes of query-row columns take part (padding columns are never written out)
+            if (mine && slot >= half && slot < 2 * half && col < ROWS) {
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt)
                     tree[(((blk - b0) * (NS / 2) + slot - half) * 16 + tt) * kWave + lane] = oacc[tt];
             }
             __syncthreads();
-            if (mine && slot < half) {
+            if (mine && slot < half && col < ROWS) {
 #pragma unroll
                 for (int tt = 0; tt < 16; ++tt)
                     oacc[tt] += tree[(((blk - b0) * (NS / 2) + slot) * 16 + tt) * kWave + lane];

@@ -479,12 +479,13 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
     }
 #pragma unroll
     for (int half = NS / 2; half >= 1; half >>= 1) {
-        if (slot >= half && slot < 2 * half) {
+        // only lanes of query-head columns take part (padding columns are never written out)
+        if (slot >= half && slot < 2 * half && n < G) {
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt) tree[slot - half][tt][lane] = oacc[tt];
         }
         __syncthreads();
-        if (slot < half) {
+        if (slot < half && n < G) {
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt) oacc[tt] += tree[slot][tt][lane];
         }
