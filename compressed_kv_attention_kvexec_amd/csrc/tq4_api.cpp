@@ -111,7 +111,7 @@ tq4_status tq4_encode_pages(const tq4_layer_pool *pool, const void *k, const voi
 
 size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t page_size) {
-    if (batch < 1 || max_seq_len < 1 || n_kv_heads < 1) return 0;
+    if (batch < 1 || batch > 65535 || max_seq_len < 1 || n_kv_heads < 1 || n_kv_heads > 65535) return 0;
     if (page_size < 32 || page_size > 1024 || page_size % 32 != 0) return 0;
     if (check_heads(n_q_heads, n_kv_heads) != TQ4_OK) return 0;
     return tq4::plan_decode(batch, max_seq_len, n_q_heads, n_kv_heads, 1).workspace_bytes;
@@ -119,7 +119,8 @@ size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_
 
 size_t tq4_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_queries, int32_t n_q_heads,
                                       int32_t n_kv_heads, int32_t page_size) {
-    if (batch < 1 || max_seq_len < 1 || n_kv_heads < 1 || n_queries < 1) return 0;
+    if (batch < 1 || batch > 65535 || max_seq_len < 1 || n_kv_heads < 1 || n_kv_heads > 65535 || n_queries < 1)
+        return 0;
     if (page_size < 32 || page_size > 1024 || page_size % 32 != 0) return 0;
     if (check_heads(n_q_heads, n_kv_heads) != TQ4_OK) return 0;
     if (int64_t{n_queries} * (n_q_heads / n_kv_heads) > TQ4_MAX_VERIFY_ROWS) return 0;
@@ -139,7 +140,8 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
     if (!q || !page_table || !seq_lens || !out) return TQ4_ERR_NULL;
     if (q_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
     if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
-    if (batch < 1 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (batch < 1 || batch > 65535 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
     if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
     if (n_queries < 1 || int64_t{n_queries} * (n_q_heads / pool->n_kv_heads) > TQ4_MAX_VERIFY_ROWS)
         return TQ4_ERR_SHAPE;
@@ -289,7 +291,9 @@ size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int
     if (page_size < 32 || page_size > 1024 || page_size % 32 != 0) return 0;
     if (check_heads(n_q_heads, n_kv_heads) != TQ4_OK) return 0;
     if (int64_t{prior_len} + chunk_len > (int64_t{1} << 31) - 1) return 0;
-    return tq4::plan_prefill(prior_len, chunk_len, n_q_heads, n_kv_heads).workspace_bytes;
+    const tq4::PrefillPlan plan = tq4::plan_prefill(prior_len, chunk_len, n_q_heads, n_kv_heads);
+    if (plan.n_qblocks > 65535 || n_kv_heads > 65535) return 0;
+    return plan.workspace_bytes;
 }
 
 tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
@@ -306,6 +310,8 @@ tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4
     if (int64_t{prior_len} + chunk_len > (int64_t{1} << 31) - 1) return TQ4_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4)) return TQ4_ERR_ALIGN;
     const tq4::PrefillPlan plan = tq4::plan_prefill(prior_len, chunk_len, n_q_heads, pool->n_kv_heads);
+    // grid (splits, query blocks, KV heads): 128 query rows per block
+    if (plan.n_qblocks > 65535 || pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
     if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return TQ4_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return TQ4_ERR_ALIGN;
     tq4::PrefillParams p{};
@@ -379,7 +385,8 @@ tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dt
     if (!q || !page_table || !seq_lens || !out) return TQ4_ERR_NULL;
     if (q_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
     if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
-    if (batch < 1 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (batch < 1 || batch > 65535 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
     if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return TQ4_ERR_ALIGN;

@@ -164,6 +164,7 @@ size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_
  *   max_seq_len: host upper bound of seq_lens, 1 <= max_seq_len <=
  *               page_table_stride * page_size; it sets the launch plan.
  *   n_q_heads : a multiple of n_kv_heads with n_q_heads / n_kv_heads <= 16.
+ *   batch, n_kv_heads: <= 65535 each (grid dimensions).
  *   scale     : softmax scale applied to q.k (1/16 = 1/sqrt(256) usually).
  *   out       : device [batch][n_q_heads][256] in q_dtype, 16-byte aligned;
  *               out[b][h] = sum_j softmax_j(scale q.k_j) v_j.
@@ -310,7 +311,8 @@ size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int
  *               prior_len + t and attends positions 0 .. prior_len + t.
  *   page_table: device int32 covering prior_len + chunk_len positions.  The
  *               chunk's own K/V must already be encoded into the pool.
- *   prior_len : >= 0; chunk_len >= 1.
+ *   prior_len : >= 0; chunk_len >= 1; chunk_len * (n_q_heads / n_kv_heads) <=
+ *               65535 * 128 (query rows, 128 per workgroup row of the grid).
  *   out       : device [chunk_len][n_q_heads][256] in q_dtype.
  *   workspace : device, >= tq4_attn_prefill_workspace_size(...) bytes,
  *               256-byte aligned, zero-filled before first use (as for decode).

@@ -225,3 +225,15 @@ def test_int8_encode_validation(lib):
     assert enc(ctypes.byref(p), FAKE, FAKE, B.TQ4_F32, FAKE + 2, 4, None) == 4
     assert enc(ctypes.byref(_i8pool(page_size=40)), FAKE, FAKE, B.TQ4_F32, FAKE, 4, None) == 2
     assert enc(ctypes.byref(p), FAKE, FAKE, B.TQ4_F32, FAKE, 0, None) == 0  # nothing to do
+
+
+def test_grid_limits_rejected_on_the_host(lib):
+    # batch and KV heads are grid dimensions (<= 65535)
+    assert _decode(lib, batch=65536, max_seq=100) == 2
+    assert _decode(lib, pool=_pool(num_pages=1, page_size=32, n_kv=65536), n_q=65536, max_seq=32, stride=1) == 2
+    assert _i8decode(lib, batch=65536, max_seq=100) == 2
+    assert lib.tq4_attn_decode_workspace_size(65536, 4000, 24, 4, 64) == 0
+    assert lib.tq4_attn_verify_workspace_size(65536, 4000, 2, 24, 4, 64) == 0
+    # prefill: 128 query rows per grid row, at most 65535 rows of workgroups
+    assert lib.tq4_attn_prefill_workspace_size(0, 65535 * 128 // 6 + 100, 24, 4, 64) == 0
+    assert lib.tq4_attn_prefill_workspace_size(0, 65535 * 128 // 6 - 100, 24, 4, 64) > 0
