@@ -237,3 +237,22 @@ def test_grid_limits_rejected_on_the_host(lib):
     # prefill: 128 query rows per grid row, at most 65535 rows of workgroups
     assert lib.tq4_attn_prefill_workspace_size(0, 65535 * 128 // 6 + 100, 24, 4, 64) == 0
     assert lib.tq4_attn_prefill_workspace_size(0, 65535 * 128 // 6 - 100, 24, 4, 64) > 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """The binding has no fallback: a missing shared library raises instead of computing
+    anything elsewhere, and the package imports no oracle code."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from compressed_kv_attention_kvexec_amd import _binding as B\n"
+        "try:\n"
+        "    B.load_library(%r)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised', 'missing' in str(e))\n"
+        "import compressed_kv_attention_kvexec_amd\n"
+        "print('oracle' in sys.modules)\n"
+    ) % (str(__import__("pathlib").Path(__file__).resolve().parents[1]), str(tmp_path / "libtq4.so"))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120).stdout.split()
+    assert out == ["raised", "True", "False"], out
