@@ -411,6 +411,44 @@ def torch_sum_read(device, gib: int = 4, reps: int = 5) -> float:
     return best
 
 
+def stream_read_probe(device, gib: int = 4, reps: int = 5) -> dict:
+    """Read rate of the streaming-read probe (libtq4probe.so, include/tq4_probe.h) over `gib` GiB,
+    best over grid sizes and `reps` repetitions: the read bandwidth this device reaches in
+    practice, the measured ceiling for memory-bound kernels."""
+    import ctypes
+    import torch
+    from compressed_kv_attention_kvexec_amd import build as hipbuild
+    lib = ctypes.CDLL(hipbuild.PROBE_LIB)
+    lib.tq4_probe_sink_words.argtypes = [ctypes.c_int32]
+    lib.tq4_probe_sink_words.restype = ctypes.c_size_t
+    lib.tq4_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p]
+    lib.tq4_probe_stream_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = {"gb_per_s": 0.0}
+    for wgs in (2048, 4096, 8192, 16384, 32768):
+        sink = torch.empty(lib.tq4_probe_sink_words(wgs), dtype=torch.int32, device=device)
+        args = (ctypes.c_void_p(x.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), wgs, stream)
+        if lib.tq4_probe_stream_read(*args) != 0:
+            raise RuntimeError("stream-read probe launch failed")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.tq4_probe_stream_read(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+            if gbs > best["gb_per_s"]:
+                best = {"gb_per_s": gbs, "workgroups": wgs}
+        del sink
+    del x
+    torch.cuda.empty_cache()
+    best["bytes"] = nbytes
+    return best
+
+
 def cpu_baseline(sample_positions: int):
     """The oracle (plain single-threaded C, fp64) on a bounded sample of the same
     workload: one layer, the first `sample_positions` cached positions, one
@@ -431,10 +469,27 @@ def cpu_baseline(sample_positions: int):
     oracle.attn_decode(pool, q, table, [sample_positions], synth.SCALE)
     dt = time.perf_counter() - t0
     per_pos_16l = dt / sample_positions * 16  # seconds per cached position over 16 layers
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": 1.0 / per_pos_16l, "unit": "positions/s", "cores": 1, "kind": "oracle",
             "sample": (f"1 layer x {sample_positions} cached positions x 24 query heads, one decode query; "
                        f"{dt:.2f} s, scaled to 16 layers"),
-            "seconds": dt}
+            "seconds": dt, "cpu_model": cpu_model, "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def calibration_copy(mib: int, dev) -> None:
+    """One device copy of `mib` MiB: the reference dispatch for scaling the PMC byte counters."""
+    import torch
+    a = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    log(f"calibration copy of {mib} MiB done")
 
 
 def main() -> int:
@@ -454,6 +509,10 @@ def main() -> int:
                     help="skip the reconstruct-then-dense-attention timing")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the uniform INT8 arm timing")
+    ap.add_argument("--only-config", default="",
+                    help="run only the cold one-layer timing of this decode workload (profiler runs)")
+    ap.add_argument("--int8-only", action="store_true",
+                    help="run only the uniform INT8 arm timing (profiler runs)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager per-layer launches instead of a HIP graph of the step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -475,6 +534,16 @@ def main() -> int:
     torch.cuda.set_device(dev)
     tq4.load_library()
     log(f"workload {w.name}: {w.n_layers} layers, seq_lens {w.seq_lens}")
+    if args.only_config:  # one cold one-layer decode workload alone, for profiler runs
+        if args.calibrate_copy_mib > 0:
+            calibration_copy(args.calibrate_copy_mib, dev)
+        print(json.dumps({"decode_config": decode_config_leg(args.only_config, dev)}), flush=True)
+        return 0
+    if args.int8_only:  # the INT8 arm alone, for profiler runs
+        if args.calibrate_copy_mib > 0:
+            calibration_copy(args.calibrate_copy_mib, dev)
+        print(json.dumps({"int8": int8_leg(w.name, dev)}), flush=True)
+        return 0
     build_stats = {}
     layers = build_layers(w, dev, build_stats)
 
@@ -489,13 +558,7 @@ def main() -> int:
     timed_layers = list(range(0, w.n_layers, EVENT_EVERY))
 
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-        log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
+        calibration_copy(args.calibrate_copy_mib, dev)
 
     def step(events=None):
         for i in range(w.n_layers):
@@ -599,6 +662,11 @@ def main() -> int:
     torch_read = torch_sum_read(dev)
     result["extra"]["torch_sum_read_gb_per_s"] = torch_read
     log(f"torch.sum over 4 GiB fp32: {torch_read:.0f} GB/s")
+    probe = stream_read_probe(dev)
+    result["extra"]["stream_read_probe"] = probe
+    result["extra"]["decode_frac_of_measured_read"] = result["roofline"]["achieved"] / probe["gb_per_s"]
+    log(f"stream-read probe over 4 GiB: {probe['gb_per_s']:.0f} GB/s ({probe['workgroups']} workgroups); "
+        f"decode call at {100 * result['extra']['decode_frac_of_measured_read']:.1f}% of it")
     if not args.no_configs:
         result["extra"]["decode_configs"] = []
         for name in ("decode_1k_p64", "decode_32k", "decode_2req_shared"):

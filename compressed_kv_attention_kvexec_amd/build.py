@@ -14,9 +14,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq4.so")
+PROBE_LIB = os.path.join(PKG, "libtq4probe.so")  # streaming-read probe (measurement support)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
+PROBE_SOURCES = ["tq4_probe.hip"]
 SOURCES = ["tq4_api.cpp", "tq4_codebook.cpp", "tq4_encode.hip", "tq4_decode.hip", "tq4_prefill.hip",
            "tq4_dense.hip", "tq4_pages.cpp", "tq4_int8.hip"]
 
@@ -43,18 +45,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC"] + objs + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libtq4.so (the attention library) and libtq4probe.so (the bandwidth probe)."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PROBE_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
