@@ -1,0 +1,88 @@
+"""Seeded sweep of random shapes through every attention entry point, each checked against the
+oracle (max |err| <= 2e-2, rel-L2 <= 5e-3): page sizes 32..512, groups 1..16, batches 1..5 with
+ragged lengths 1..4,000 (and empty requests), verifier k = 1..8 within the 48-row limit, prefill
+chunks 1..160 over 0..1,500 cached positions, and the INT8 and unfused paths."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _pools import bf16_queries, int8_to_device, oracle_int8_pool, oracle_pool, parity, to_device
+
+pytestmark = pytest.mark.gpu
+
+PAGES = (32, 64, 128, 256, 512)
+GROUPS = ((24, 4), (16, 16), (8, 4), (12, 4), (64, 4), (6, 1), (32, 2))
+PREFILL_GROUPS = ((24, 4), (8, 4), (12, 4), (6, 1), (32, 2))  # the oracle decodes every key per row
+
+
+def _decode_case(rng, i):
+    page = int(rng.choice(PAGES))
+    n_q, n_kv = GROUPS[int(rng.integers(len(GROUPS)))]
+    batch = int(rng.integers(1, 6))
+    lens = tuple(int(x) for x in rng.integers(0, 4001, batch))
+    if batch > 1 and i % 4 == 3:
+        lens = lens[:-1] + (0,)  # an empty request among others
+    if max(lens) == 0:
+        lens = (1,) + lens[1:]
+    pages = sum(-(-L // page) for L in lens) + int(rng.integers(0, 4))
+    w = synth.Workload(200 + i, f"sweep{i}", "decode", 1, page, max(pages, 1), seq_lens=lens, n_q=n_q, n_kv=n_kv)
+    return w
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_sweep_decode_verify_int8(i):
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    rng = np.random.default_rng(1000 + i)
+    w = _decode_case(rng, i)
+    pool, table = oracle_pool(w)
+    dpool = to_device(pool)
+    tab = torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda()
+    seq = torch.tensor(w.seq_lens, dtype=torch.int32).cuda()
+    max_seq = max(w.seq_lens)
+    what = f"case {i}: page {w.page_size}, n_q {w.n_q}, n_kv {w.n_kv}, lens {w.seq_lens}"
+    # decode
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    out = tq4.tq4_attn_decode(dpool, q_t.cuda(), tab, seq, max_seq, synth.SCALE)
+    torch.cuda.synchronize()
+    parity(out.cpu(), oracle.attn_decode(pool, q64, table, w.seq_lens, synth.SCALE), "decode " + what)
+    # verifier with a random k inside the row limit
+    G = w.n_q // w.n_kv
+    k = int(rng.integers(1, max(1, min(8, 48 // G)) + 1))
+    qv, qv64 = bf16_queries(w, 1, w.batch * k)
+    qv = qv.reshape(w.batch, k, w.n_q, 256).contiguous()
+    qv64 = qv64.reshape(w.batch, k, w.n_q, 256)
+    outv = tq4.tq4_attn_verify(dpool, qv.cuda(), tab, seq, max_seq, synth.SCALE)
+    torch.cuda.synchronize()
+    parity(outv.cpu(), oracle.attn_verify(pool, qv64, table, w.seq_lens, synth.SCALE), f"verify k={k} " + what)
+    # INT8 arm on the same placement
+    pool8, _ = oracle_int8_pool(w, table=table)
+    out8 = tq4.tq4_int8_attn_decode(int8_to_device(pool8), q_t.cuda(), tab, seq, max_seq, synth.SCALE)
+    torch.cuda.synchronize()
+    parity(out8.cpu(), oracle.int8_attn_decode(pool8, q64, table, w.seq_lens, synth.SCALE), "int8 " + what)
+    # unfused chain against attention over the pages
+    kd, vd = tq4.tq4_reconstruct_pages(dpool, tab, seq, max_seq)
+    outs = tq4.tq4_sdpa_decode(q_t.cuda(), kd, vd, seq, synth.SCALE)
+    torch.cuda.synchronize()
+    parity(outs.cpu(), oracle.attn_decode(pool, q64, table, w.seq_lens, synth.SCALE), "unfused " + what)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_sweep_prefill(i):
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    rng = np.random.default_rng(2000 + i)
+    page = int(rng.choice(PAGES))
+    n_q, n_kv = PREFILL_GROUPS[int(rng.integers(len(PREFILL_GROUPS)))]
+    prior = int(rng.integers(0, 1501))
+    chunk = int(rng.integers(1, 161))
+    w = synth.Workload(300 + i, f"pfsweep{i}", "prefill", 1, page, -(-(prior + chunk) // page) + 2,
+                       prior_len=prior, chunk_len=chunk, n_q=n_q, n_kv=n_kv)
+    pool, table = oracle_pool(w)
+    q_t, q64 = bf16_queries(w, 0, chunk)
+    out = tq4.tq4_attn_prefill_chunk(to_device(pool), q_t.cuda(), torch.from_numpy(table[0]).cuda(), prior,
+                                     synth.SCALE)
+    torch.cuda.synchronize()
+    ref = oracle.attn_prefill_rows(pool, q64, np.arange(chunk), table[0], prior, synth.SCALE)
+    parity(out.cpu(), ref, f"prefill case {i}: page {page}, n_q {n_q}, n_kv {n_kv}, prior {prior}, chunk {chunk}")
