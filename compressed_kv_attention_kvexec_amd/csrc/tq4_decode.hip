@@ -305,16 +305,13 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
             kn[4 * h + 2] = f16lo(kr.kn[h].y);
             kn[4 * h + 3] = f16hi(kr.kn[h].y);
         }
-        // x = (q_rot . c[idx]) n_k; the score in log2 units is fcol x.  Masked keys get -inf.
+        // x = (q_rot . c[idx]) n_k; the score in log2 units is fcol x.  Masked keys get -inf (below).
         float xs[8];
         const int lim = valid ? (min(key_end, lim_col) - key0) : 0;  // keys at offset >= lim are masked
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int koff = 16 * h + 4 * gq + r;
-                xs[4 * h + r] = (koff < lim) ? sacc[h][r] * kn[4 * h + r] : -INFINITY;
-            }
+            for (int r = 0; r < 4; ++r) xs[4 * h + r] = sacc[h][r] * kn[4 * h + r];
         const int64_t rec = rec_of(t + NS, inext, valid_t);
         const int64_t rec_pf = live ? rec : 0;
         const LaneOffsets ofs_pf = live ? lofs : dead_ofs;
@@ -335,10 +332,17 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
             nv[4 * h + 2] = f16lo(vr.vn[h].y);
             nv[4 * h + 3] = f16hi(vr.vn[h].y);
         }
-        // a masked key's record (past the length, or never written) may hold any bits: its norm
-        // is dropped here, since exp2(-inf) * NaN would not be 0
+        // Masking, only for tiles some column does not see in full (in place, so the common path
+        // has no copies): score -inf, and value norm 0, since a masked key's record (past the
+        // length, or never written) may hold any bits and exp2(-inf) * NaN would not be 0.
+        if (!__all(lim >= kTile)) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) nv[j] = ((j < 4 ? 4 * gq + j : 12 + 4 * gq + j) < lim) ? nv[j] : 0.f;
+            for (int j = 0; j < 8; ++j)
+                if ((j < 4 ? 4 * gq + j : 12 + 4 * gq + j) >= lim) {
+                    xs[j] = -INFINITY;
+                    nv[j] = 0.f;
+                }
+        }
         float mx = xs[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, xs[j]);

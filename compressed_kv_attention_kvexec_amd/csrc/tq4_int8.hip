@@ -385,10 +385,7 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int koff = 16 * h + 4 * gq + r;
-                xs[4 * h + r] = (koff < lim) ? sacc[h][r] * ksc[4 * h + r] : -INFINITY;
-            }
+            for (int r = 0; r < 4; ++r) xs[4 * h + r] = sacc[h][r] * ksc[4 * h + r];
         const int64_t rec = rec_of(t + NS, inext, valid_t);
         const int64_t rec_pf = live ? rec : 0;
         const I8LaneOffsets ofs_pf = live ? lofs : dead_ofs;
@@ -399,6 +396,22 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
             __builtin_amdgcn_s_setprio(1);
         else
             __builtin_amdgcn_s_setprio(0);
+        // value scales of the tile's keys as fp16 pairs (keys sigma(2i), sigma(2i + 1))
+        u32x2 vn[2] = {vr.vn[0], vr.vn[1]};
+        // Masking, only in a tile that is not visible in full (in place, so the common path has no
+        // copies): score -inf, value scale 0 -- the records of masked keys (past the length, or
+        // never written) may hold any bits, and code * scale must be an exact 0 for them.
+        if (!__all(lim >= kTile)) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k0 = 16 * h + 4 * gq;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (k0 + r >= lim) xs[4 * h + r] = -INFINITY;
+                vn[h].x &= (k0 < lim ? 0xffffu : 0u) | (k0 + 1 < lim ? 0xffff0000u : 0u);
+                vn[h].y &= (k0 + 2 < lim ? 0xffffu : 0u) | (k0 + 3 < lim ? 0xffff0000u : 0u);
+            }
+        }
         float mx = xs[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, xs[j]);
@@ -427,15 +440,6 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
         pr.y = pack_f16x2(pv[2], pv[3]);
         pr.z = pack_f16x2(pv[4], pv[5]);
         pr.w = pack_f16x2(pv[6], pv[7]);
-        // value scales of masked keys are zeroed: their records (past the length, or never
-        // written) may hold any bits, and code * scale must be an exact 0 for them
-        u32x2 vn[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int k0 = 16 * h + 4 * gq;
-            vn[h].x = vr.vn[h].x & ((k0 < lim ? 0xffffu : 0u) | (k0 + 1 < lim ? 0xffff0000u : 0u));
-            vn[h].y = vr.vn[h].y & ((k0 + 2 < lim ? 0xffffu : 0u) | (k0 + 3 < lim ? 0xffff0000u : 0u));
-        }
         VSteps<0, 16>::run(vr.v, vn, __builtin_bit_cast(half8, pr), oacc);
         __builtin_amdgcn_sched_barrier(0);
         i8_load_v(p, rec_pf, ofs_pf, vr);

@@ -285,11 +285,24 @@ void tq4_prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int lim = valid ? min(key_end, lim_row[j]) - key0 : 0;  // visible keys in this tile
-            float xs[8];
+            // Most tiles are visible to every row of the block: those skip the per-key masking.
+            // Otherwise masked keys get score -inf and value norm 0 (their records, past the cached
+            // length, may hold any bits, NaN norms included).
+            float xs[8], nvm[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int koff = (q < 4) ? (4 * gq + q) : (16 + 4 * gq + (q - 4));
-                xs[q] = (koff < lim) ? sacc[j][q >> 2][q & 3] * kn[q] : -INFINITY;
+                xs[q] = sacc[j][q >> 2][q & 3] * kn[q];
+                nvm[q] = nv[q];
+            }
+            if (!__all(lim >= kTile)) {  // masked in place, so the common path has no copies
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int koff = (q < 4) ? (4 * gq + q) : (16 + 4 * gq + (q - 4));
+                    if (koff >= lim) {
+                        xs[q] = -INFINITY;
+                        nvm[q] = 0.f;
+                    }
+                }
             }
             float mx = xs[0];
 #pragma unroll
@@ -321,9 +334,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
             for (int q = 0; q < 8; ++q) {
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[q], fcol[j], neg_m));
                 l_run[j] += e;
-                // masked keys past the cached length may hold any bits, NaN norms included
-                const int koff = (q < 4) ? (4 * gq + q) : (16 + 4 * gq + (q - 4));
-                pv[q] = (koff < lim) ? e * nv[q] : 0.f;
+                pv[q] = e * nvm[q];
             }
             u32x4 pr;
             pr.x = pack_f16x2(pv[0], pv[1]);

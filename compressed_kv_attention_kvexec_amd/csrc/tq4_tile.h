@@ -72,8 +72,11 @@ __device__ __forceinline__ void nibble_transpose8(const uint32_t in[8], uint32_t
 __device__ __forceinline__ float f16lo(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w)); }
 __device__ __forceinline__ float f16hi(uint32_t w) { return f16_bits_to_f32(static_cast<uint16_t>(w >> 16)); }
 
+// Two fp32 -> packed fp16 (lo in the low half) with one v_cvt_pk_f16_f32, round to nearest even:
+// the same bits as two f32_to_f16_bits conversions.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_f16_bits(lo)) | (static_cast<uint32_t>(f32_to_f16_bits(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, f16x2_t));
 }
 
 // First record of a tile (page `pid`, in-page offset of key0); page IDs outside the pool map to
