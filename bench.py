@@ -322,6 +322,27 @@ def int8_leg(name: str, device, reps: int = 20) -> dict:
     pages = sum(-(-L // w.page_size) for L in w.seq_lens)
     positions = sum(w.seq_lens)
     nbytes = positions * INT8_BYTES_PER_POS_LAYER + w.batch * w.n_q * 256 * 2 * 2 + pages * 4 + w.batch * 4
+    # the packed verifier over the same INT8 pages: the last k positions of each request
+    verify = []
+    for k in (2, 4, 8):
+        qv = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (w.batch, k, w.n_q, 256), device).to(torch.bfloat16)
+        outv = torch.empty_like(qv)
+        wsv = tq4.new_workspace(tq4.tq4_int8_attn_verify_workspace_size(w.batch, max(w.seq_lens), k, w.n_q, w.n_kv,
+                                                                        w.page_size), device)
+        vcall = tq4.prepare_int8_verify(pool, qv, tab, seq, max(w.seq_lens), synth.SCALE, outv, wsv)
+        for _ in range(2):
+            vcall()
+        vt = []
+        for _ in range(reps // 2):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vcall()
+            e1.record()
+            torch.cuda.synchronize()
+            vt.append(e0.elapsed_time(e1) / 1e3)
+        tv = sorted(vt)[len(vt) // 2]
+        verify.append({"n_queries": k, "us_per_call": tv * 1e6, "query_tokens_per_s": w.batch * k / tv})
     # encoder: 32,768 tokens of fp32 K and V
     tokens = 32768
     k = synth.torch_normal(synth.seed_of(w.wid, 1, synth.T_K), (tokens, w.n_kv, 256), device)
@@ -344,6 +365,7 @@ def int8_leg(name: str, device, reps: int = 20) -> dict:
             "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
             "int8_bytes_per_position_layer": INT8_BYTES_PER_POS_LAYER,
             "encode_vectors_per_s": tokens * w.n_kv * 2 / te, "encode_gb_per_s": enc_bytes / te / 1e9,
+            "verify": verify,
             "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
 
 
@@ -695,7 +717,8 @@ def main() -> int:
         r["int8_over_tq4"] = r["us_per_call"] / tq4_cold["us_per_call"]
         result["extra"]["int8"] = r
         log(f"int8 arm: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s (cold); TQ4 cold "
-            f"{r['tq4_cold_us_per_call']:.1f} us ({r['int8_over_tq4']:.2f}x); encode {r['encode_gb_per_s']:.0f} GB/s")
+            f"{r['tq4_cold_us_per_call']:.1f} us ({r['int8_over_tq4']:.2f}x); encode {r['encode_gb_per_s']:.0f} GB/s; "
+            f"verify k=2/4/8 " + " / ".join(f"{v['us_per_call']:.1f}" for v in r["verify"]) + " us")
     if not args.no_prefill:
         log("prefill leg ...")
         result["extra"]["prefill"] = prefill_leg(dev)

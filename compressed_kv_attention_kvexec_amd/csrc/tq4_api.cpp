@@ -372,11 +372,17 @@ size_t tq4_int8_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, i
     return tq4_attn_decode_workspace_size(batch, max_seq_len, n_q_heads, n_kv_heads, page_size);
 }
 
-tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype,
-                                const int32_t *page_table, int32_t page_table_stride,
-                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
-                                int32_t n_q_heads, float scale, void *out, void *workspace,
-                                size_t workspace_bytes, void *stream) {
+size_t tq4_int8_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_queries,
+                                           int32_t n_q_heads, int32_t n_kv_heads, int32_t page_size) {
+    return tq4_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q_heads, n_kv_heads, page_size);
+}
+
+namespace {
+
+tq4_status int8_common(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,
+                       const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
+                       int32_t batch, int32_t max_seq_len, int32_t n_q_heads, float scale, void *out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
     tq4_status st = check_int8_pool(pool);
     if (st != TQ4_OK) return st;
     if (!pool->k_codes || !pool->v_codes || !pool->k_scales || !pool->v_scales) return TQ4_ERR_NULL;
@@ -388,9 +394,11 @@ tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dt
     if (batch < 1 || batch > 65535 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
     if (pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
     if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
+    if (n_queries < 1 || int64_t{n_queries} * (n_q_heads / pool->n_kv_heads) > TQ4_MAX_VERIFY_ROWS)
+        return TQ4_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return TQ4_ERR_ALIGN;
-    const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads, 1);
+    const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads, n_queries);
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return TQ4_ERR_WORKSPACE;
     if (workspace != nullptr && !aligned(workspace, 256)) return TQ4_ERR_ALIGN;
@@ -413,6 +421,26 @@ tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dt
     p.out = static_cast<uint16_t *>(out);
     p.workspace = workspace;
     return from_hip(tq4::launch_int8_decode(p, plan, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype,
+                                const int32_t *page_table, int32_t page_table_stride,
+                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                int32_t n_q_heads, float scale, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    return int8_common(pool, q, q_dtype, 1, page_table, page_table_stride, seq_lens, batch, max_seq_len,
+                       n_q_heads, scale, out, workspace, workspace_bytes, stream);
+}
+
+tq4_status tq4_int8_attn_verify(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,
+                                const int32_t *page_table, int32_t page_table_stride,
+                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                int32_t n_q_heads, float scale, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    return int8_common(pool, q, q_dtype, n_queries, page_table, page_table_stride, seq_lens, batch, max_seq_len,
+                       n_q_heads, scale, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,15 +1,17 @@
-// tq4_int8.hip -- the uniform INT8 KV arm on gfx950: encoder and single-query decode attention over
-// INT8 pages ("Fitting a 27B-Parameter LLM into 24 GiB of Laptop Memory", section "Reasoning at
-// 200K: 29 of 30 AIME Problems": a uniform INT8 KV cache is the comparison arm of the TQ4 run).
+// tq4_int8.hip -- the uniform INT8 KV arm on gfx950: encoder, and decode attention over INT8 pages
+// for one query token per request or its last n_queries tokens (the packed verifier) ("Fitting a
+// 27B-Parameter LLM into 24 GiB of Laptop Memory", section "Reasoning at 200K: 29 of 30 AIME
+// Problems": a uniform INT8 KV cache is the comparison arm of the TQ4 run).
 //
 // Record (the page fixes no format; this is the plain per-vector reading): 256 signed codes q_d in
 // [-127, 127] and one fp16 scale s; the vector is q * s in the natural domain (no rotation).
 // Encoding, fp32 with round to nearest even: s = fp16(max_d |x_d| / 127), q_d = clamp(rint(x_d / s),
 // -127, 127), every code 0 when s == 0.
 //
-// Decode attention keeps the work decomposition of the TQ4 decode kernel: grid (split, KV head,
-// request); the G query heads of a KV head are the 16 MFMA columns; the 8 wavefronts of a split
-// take every 8th 32-key tile, two per SIMD.  Per tile and wavefront:
+// Attention keeps the work decomposition of the TQ4 decode kernel: grid (split, KV head, request);
+// the query rows of a KV head (G heads x n_queries tokens) are MFMA columns, 16 per block; a
+// wavefront owns one block and every NS-th 32-key tile of its split (decode: one block, 8
+// wavefronts, two per SIMD).  Per tile and wavefront:
 //   S^T[32 keys][16] = C_K . Q^T       codes -> fp16 exactly     16 x v_mfma_f32_16x16x32_f16
 //   x_j = S_j s_k,j, online softmax in base 2 (lazy rescale as in the TQ4 kernel)
 //   O^T[256][16] += (C_V s_v)^T . P^T  each value code * scale rounded once to fp16, 16 MFMAs
@@ -137,12 +139,13 @@ hipError_t launch_int8_encode(const Int8EncodeParams &p, hipStream_t stream) {
 
 // ---------------------------------------------------------------- decode attention
 
-constexpr int kI8Waves = 8;
 constexpr float kI8RescaleSlack = 8.0f;  // log2 headroom before the running maximum is moved
 
 struct Int8DecodeArgs {
     Int8DecodeParams p;
     int32_t group;
+    int32_t n_queries;  // query tokens per request (1: decode)
+    int32_t rows;       // n_queries * group
     int32_t n_splits;
     int32_t split_tiles;
     int32_t partial_floats;
@@ -245,29 +248,46 @@ __device__ __forceinline__ void i8_load_v(const Int8DecodeParams &p, int64_t rec
     for (int h = 0; h < 2; ++h) t.vn[h] = *reinterpret_cast<const u32x2 *>(sb + o.nrm + 32u * h);
 }
 
-__global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8DecodeArgs a) {
-    constexpr int NS = kI8Waves;
-    constexpr int NT = NS * kWave;
-    __shared__ __align__(16) half8 qop_sh[8][kWave];  // query operand per K-step and lane
-    __shared__ __align__(16) float4v tree[NS / 2][16][kWave];
-    __shared__ float stat_m[NS][16];
-    __shared__ float stat_l[NS][16];
-    __shared__ float row_f[16];
-    __shared__ float resL[16];
-    __shared__ int32_t progress[NS];
+// The query rows of one (request, KV head) -- row r = i G + h for query token i of n_queries and
+// head h of the group -- fill NB blocks of 16 MFMA columns; wavefront w = blk NS + slot owns
+// column block blk and every NS-th tile from its slot, so the NB wavefronts of a slot read the
+// same tiles (the caches serve all but the first).  Decode is NB = 1, NS = 8; the multi-query
+// verifier uses NB = 2, NS = 4 and NB = 3, NS = 2.  Column r of query token i sees positions
+// 0 .. L - KQ + i.
+template <int NB, int NS>
+__global__ __launch_bounds__(NB * NS * kWave) void tq4_int8_split_kernel(Int8DecodeArgs a) {
+    constexpr int NW = NB * NS;
+    constexpr int NT = NW * kWave;
+    constexpr int NCOL = 16 * NB;
+    constexpr int kTreeBlocks = 8 / NS;  // blocks merged per round: [blocks][NS / 2][16][64] rows
+    __shared__ __align__(16) half8 qop_sh[NB][8][kWave];  // query operand per block, K-step, lane
+    __shared__ __align__(16) float4v tree[kTreeBlocks][NS / 2][16][kWave];
+    __shared__ float stat_m[NW][16];
+    __shared__ float stat_l[NW][16];
+    __shared__ float row_f[NCOL];
+    __shared__ float resL[NCOL];
+    __shared__ float resM[NCOL];
+    __shared__ int32_t progress[NW];
 
     const Int8DecodeParams &p = a.p;
     const int G = a.group;
+    const int KQ = a.n_queries;
+    const int ROWS = a.rows;  // KQ * G <= NCOL
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
 
     const int L_req = p.seq_lens[b];
-    const int slot = __builtin_amdgcn_readfirstlane(wave);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int slot = wave_u % NS, blk = wave_u / NS;
     const int split_keys = a.split_tiles * kTile;
     const int key_begin = s * split_keys;
     const int32_t *pt_row = p.page_table + static_cast<int64_t>(b) * p.table_stride;
-    auto row_off = [&](int h) -> int64_t { return (static_cast<int64_t>(b) * p.n_q + static_cast<int64_t>(g) * G + h) * kDim; };
+    // element offset of query row r (token i, head h) in q and out: [request][token][q head][256]
+    auto row_off = [&](int r) -> int64_t {
+        const int i = r / G, h = r - i * G;
+        return ((static_cast<int64_t>(b) * KQ + i) * p.n_q + static_cast<int64_t>(g) * G + h) * kDim;
+    };
 
     int pid_vec = 0;
     auto fetch_pids = [&](int chunk) {
@@ -296,9 +316,8 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // query rows, page IDs and the first tile are requested before the length is known
-    const u32x2 q_raw0 = *reinterpret_cast<const u32x2 *>(p.q + row_off(min(slot, G - 1)) + 4 * lane);
-    const u32x2 q_raw1 = *reinterpret_cast<const u32x2 *>(p.q + row_off(min(slot + NS, G - 1)) + 4 * lane);
+    // query row, page IDs and the first tile are requested before the length is known
+    const u32x2 q_raw0 = *reinterpret_cast<const u32x2 *>(p.q + row_off(min(wave_u, ROWS - 1)) + 4 * lane);
     fetch_pids(0);
     issue(slot, 0, true);
 
@@ -306,16 +325,16 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
     const int n_active = (L + split_keys - 1) / split_keys;
     if (s >= n_active) {
         if (L == 0 && s == 0)
-            for (int i = tid; i < G * kDim; i += NT) p.out[row_off(i / kDim) + (i % kDim)] = 0;
+            for (int i = tid; i < ROWS * kDim; i += NT) p.out[row_off(i / kDim) + (i % kDim)] = 0;
         return;
     }
     const int key_end = min(key_begin + split_keys, L);
     const int n_tiles = (key_end - key_begin + kTile - 1) / kTile;
     const int n_mine = slot < n_tiles ? (n_tiles - slot + NS - 1) / NS : 0;
 
-    // ---- query operand: column r (query head r of the group) is written by wavefront r % 8; a
-    // power-of-two scale puts max |q| in [2^13, 2^14) for the fp16 operand
-    if (tid < NS) progress[tid] = 0;
+    // ---- query operand: column r (a query row) is written by wavefront r % NW; a power-of-two
+    // scale puts max |q| in [2^13, 2^14) for the fp16 operand; padding columns are zeroed
+    if (tid < NW) progress[tid] = 0;
     auto put_row = [&](int r, u32x2 raw) {
         const float y[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
                             __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
@@ -324,21 +343,35 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
         if (lane == 0) row_f[r] = p.scale * 1.4426950408889634f * ldexpf(1.0f, -e);
         // dims 4 l .. 4 l + 3: K-step 2 (l / 16) + (l / 2) % 2, lane group (l / 4) % 4, bytes 8 (l % 2)
         const int ks = 2 * (lane >> 4) + ((lane >> 1) & 1);
-        const int dst_lane = 16 * ((lane >> 2) & 3) + r;
+        const int dst_lane = 16 * ((lane >> 2) & 3) + (r & 15);
         u32x2 hv;
         hv.x = pack_f16x2(y[0] * qs, y[1] * qs);
         hv.y = pack_f16x2(y[2] * qs, y[3] * qs);
-        *reinterpret_cast<u32x2 *>(reinterpret_cast<char *>(&qop_sh[ks][dst_lane]) + 8 * (lane & 1)) = hv;
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<char *>(&qop_sh[r >> 4][ks][dst_lane]) + 8 * (lane & 1)) = hv;
     };
     auto zero_column = [&](int r) {
-        if (lane < 32) reinterpret_cast<u32x4 *>(&qop_sh[lane & 7][16 * (lane >> 3) + r])[0] = u32x4{0u, 0u, 0u, 0u};
+        if (lane < 32)
+            reinterpret_cast<u32x4 *>(&qop_sh[r >> 4][lane & 7][16 * (lane >> 3) + (r & 15)])[0] = u32x4{0u, 0u, 0u, 0u};
     };
-    if (slot < G) put_row(slot, q_raw0); else zero_column(slot);
-    if (slot + NS < G) put_row(slot + NS, q_raw1); else zero_column(slot + NS);
+    if (wave_u < ROWS)
+        put_row(wave_u, q_raw0);
+    else
+        zero_column(wave_u);
+    for (int r = wave_u + NW; r < NCOL; r += NW) {
+        if (r < ROWS)
+            put_row(r, *reinterpret_cast<const u32x2 *>(p.q + row_off(r) + 4 * lane));
+        else
+            zero_column(r);
+    }
     __syncthreads();
 
-    const float fcol = n < G ? row_f[n] : 1.f;
-    const half8 *qop = &qop_sh[0][lane];
+    // this lane's column r = 16 blk + n: score factor and causal limit (padding columns see every
+    // key and are never written)
+    const int col = 16 * blk + n;
+    const bool live_col = col < ROWS;
+    const float fcol = live_col ? row_f[col] : 1.f;
+    const int lim_col = live_col ? L - KQ + col / G + 1 : L;
+    const half8 *qop = &qop_sh[blk][0][lane];
 
     float4v oacc[16];
 #pragma unroll
@@ -348,11 +381,15 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
     // Issue priority of the pair of wavefronts on one SIMD (w and w ^ 4), as in the TQ4 kernel:
     // the younger takes the higher priority while not ahead of its partner, the older only while
     // behind.  Tile assignment is static, so results do not depend on timing.
-    const int partner = slot ^ (NS / 2);
-    const bool younger = slot >= NS / 2;
+    constexpr bool kPaired = NW == 8;
+    const int partner = wave_u ^ (NW / 2);
+    const bool younger = wave_u >= NW / 2;
     auto step = [&](int t, int inext, bool live, int done) {
-        if (lane == 0) progress[slot] = done;
-        const int other = __builtin_amdgcn_readfirstlane(progress[partner]);
+        int other = 0;
+        if constexpr (kPaired) {
+            if (lane == 0) progress[wave_u] = done;
+            other = __builtin_amdgcn_readfirstlane(progress[partner]);
+        }
         const int key0 = key_begin + t * kTile;
         const bool valid = valid_t;
         float4v sacc[2];
@@ -381,7 +418,7 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
             ksc[4 * h + 3] = f16hi(kr.kn[h].y);
         }
         float xs[8];
-        const int lim = valid ? (key_end - key0) : 0;
+        const int lim = valid ? (min(key_end, lim_col) - key0) : 0;  // keys at offset >= lim are masked
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -392,24 +429,29 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
         __builtin_amdgcn_sched_barrier(0);
         i8_load_k(p, rec_pf, ofs_pf, kr);
         __builtin_amdgcn_sched_barrier(0);
-        if (younger ? (done <= other) : (done < other))
-            __builtin_amdgcn_s_setprio(1);
-        else
-            __builtin_amdgcn_s_setprio(0);
+        if constexpr (kPaired) {
+            if (younger ? (done <= other) : (done < other))
+                __builtin_amdgcn_s_setprio(1);
+            else
+                if constexpr (kPaired) __builtin_amdgcn_s_setprio(0);
+        }
         // value scales of the tile's keys as fp16 pairs (keys sigma(2i), sigma(2i + 1))
         u32x2 vn[2] = {vr.vn[0], vr.vn[1]};
         // Masking, only in a tile that is not visible in full (in place, so the common path has no
-        // copies): score -inf, value scale 0 -- the records of masked keys (past the length, or
-        // never written) may hold any bits, and code * scale must be an exact 0 for them.
+        // copies).  A key outside this lane's column's limit gets score -inf (so P = 0).  A key past
+        // the request's length (or on an invalid page) also gets value scale 0: its record may
+        // hold any bits, and code * scale must be an exact 0.  The value operand is shared by every
+        // column, so only that column-independent limit may touch it.
         if (!__all(lim >= kTile)) {
+            const int lim_v = valid ? (key_end - key0) : 0;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int k0 = 16 * h + 4 * gq;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (k0 + r >= lim) xs[4 * h + r] = -INFINITY;
-                vn[h].x &= (k0 < lim ? 0xffffu : 0u) | (k0 + 1 < lim ? 0xffff0000u : 0u);
-                vn[h].y &= (k0 + 2 < lim ? 0xffffu : 0u) | (k0 + 3 < lim ? 0xffff0000u : 0u);
+                vn[h].x &= (k0 < lim_v ? 0xffffu : 0u) | (k0 + 1 < lim_v ? 0xffff0000u : 0u);
+                vn[h].y &= (k0 + 2 < lim_v ? 0xffffu : 0u) | (k0 + 3 < lim_v ? 0xffff0000u : 0u);
             }
         }
         float mx = xs[0];
@@ -455,58 +497,66 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
         }
         for (int i = 0; i < cn; ++i) step(tc + i * NS, i + 1, i + 1 < cn, c0 + i);
     }
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (kPaired) __builtin_amdgcn_s_setprio(0);
 
-    // ---- merge the wavefronts: rescale to the workgroup maximum, then a fixed-order tree in LDS
+    // ---- merge the wavefronts of each block: rescale to the block maximum, then a fixed-order
+    // tree in LDS, kTreeBlocks blocks at a time (only query-row lanes take part)
     float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
     l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
     if (gq == 0) {
-        stat_m[slot][n] = m_run;
-        stat_l[slot][n] = l_tot;
+        stat_m[wave_u][n] = m_run;
+        stat_l[wave_u][n] = l_tot;
     }
     __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[j][n]);
     {
+        float M = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[blk * NS + j][n]);
         const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) oacc[tt] *= f;
     }
-    if (tid < 16) {
+    if (tid < NCOL) {
+        const int cb = tid >> 4, cn = tid & 15;
+        float M = -INFINITY;
+        for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[cb * NS + j][cn]);
         float Ls = 0.f;
         for (int j = 0; j < NS; ++j) {
-            const float mj = stat_m[j][tid];
-            Ls += (mj == -INFINITY) ? 0.f : stat_l[j][tid] * __builtin_amdgcn_exp2f(mj - M);
+            const float mj = stat_m[cb * NS + j][cn];
+            Ls += (mj == -INFINITY) ? 0.f : stat_l[cb * NS + j][cn] * __builtin_amdgcn_exp2f(mj - M);
         }
+        resM[tid] = M;
         resL[tid] = Ls;
     }
 #pragma unroll
-    for (int half = NS / 2; half >= 1; half >>= 1) {
-        // only lanes of query-head columns take part (padding columns are never written out)
-        if (slot >= half && slot < 2 * half && n < G) {
+    for (int b0 = 0; b0 < NB; b0 += kTreeBlocks) {
+        const bool mine = blk >= b0 && blk < b0 + kTreeBlocks && live_col;
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt) tree[slot - half][tt][lane] = oacc[tt];
-        }
-        __syncthreads();
-        if (slot < half && n < G) {
+        for (int half = NS / 2; half >= 1; half >>= 1) {
+            if (mine && slot >= half && slot < 2 * half) {
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt) oacc[tt] += tree[slot][tt][lane];
+                for (int tt = 0; tt < 16; ++tt) tree[blk - b0][slot - half][tt][lane] = oacc[tt];
+            }
+            __syncthreads();
+            if (mine && slot < half) {
+#pragma unroll
+                for (int tt = 0; tt < 16; ++tt) oacc[tt] += tree[blk - b0][slot][tt][lane];
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
-    if (slot != 0 || n >= G) return;
+    if (slot != 0 || !live_col) return;
 
-    // lane (gq, n), register r of M-tile e: dim 16 (4 gq + r) + e of column n
+    // lane (gq, n), register r of M-tile e: dim 16 (4 gq + r) + e of column col
     if (n_active > 1) {
         const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
         float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
                      (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
         if (gq == 0) {
-            dst[n] = M;
-            dst[kSplitStatPad + n] = resL[n];
+            dst[col] = resM[col];
+            dst[kSplitStatPad + col] = resL[col];
         }
-        float *row = dst + 2 * kSplitStatPad + n * kDim;
+        float *row = dst + 2 * kSplitStatPad + col * kDim;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float *d = row + 16 * (4 * gq + r);
@@ -518,9 +568,9 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
         return;
     }
     // single split: o = O / L straight to the output
-    const float Lh = resL[n];
+    const float Lh = resL[col];
     const float f = Lh > 0.f ? 1.0f / Lh : 0.f;
-    uint16_t *orow = p.out + row_off(n);
+    uint16_t *orow = p.out + row_off(col);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         u32x4 o0, o1;
@@ -539,16 +589,29 @@ __global__ __launch_bounds__(kI8Waves * kWave) void tq4_int8_split_kernel(Int8De
 }
 
 hipError_t launch_int8_decode(const Int8DecodeParams &p, const DecodePlan &plan, hipStream_t stream) {
-    if (plan.col_blocks != 1 || plan.n_queries != 1 || plan.slots != kI8Waves) return hipErrorInvalidValue;
     Int8DecodeArgs a;
     a.p = p;
     a.group = plan.group;
+    a.n_queries = plan.n_queries;
+    a.rows = plan.rows;
     a.n_splits = plan.n_splits;
     a.split_tiles = plan.split_tiles;
     a.partial_floats = static_cast<int32_t>(plan.partial_floats);
     a.parts_off = plan.counters_bytes;
     const dim3 grid(plan.n_splits, p.n_kv, p.batch);
-    hipLaunchKernelGGL(tq4_int8_split_kernel, grid, dim3(kI8Waves * kWave), 0, stream, a);
+    switch (plan.col_blocks) {
+        case 1:
+            hipLaunchKernelGGL((tq4_int8_split_kernel<1, 8>), grid, dim3(8 * kWave), 0, stream, a);
+            break;
+        case 2:
+            hipLaunchKernelGGL((tq4_int8_split_kernel<2, 4>), grid, dim3(8 * kWave), 0, stream, a);
+            break;
+        case 3:  // 12 wavefronts would leave 168 registers each and spill; 6 fit without
+            hipLaunchKernelGGL((tq4_int8_split_kernel<3, 2>), grid, dim3(6 * kWave), 0, stream, a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     if (plan.n_splits > 1) {
         CombineArgs c;
         c.parts = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + plan.counters_bytes);
@@ -560,7 +623,7 @@ hipError_t launch_int8_decode(const Int8DecodeParams &p, const DecodePlan &plan,
         c.partial_floats = static_cast<int32_t>(plan.partial_floats);
         c.rows = plan.rows;
         c.group = plan.group;
-        c.n_queries = 1;
+        c.n_queries = plan.n_queries;
         c.n_q = p.n_q;
         c.n_kv = p.n_kv;
         c.batch = p.batch;

@@ -373,6 +373,23 @@ tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dt
                                 int32_t n_q_heads, float scale, void *out, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* Workspace bytes tq4_int8_attn_verify needs (as tq4_attn_verify_workspace_size). */
+size_t tq4_int8_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_queries,
+                                           int32_t n_q_heads, int32_t n_kv_heads, int32_t page_size);
+
+/* tq4_int8_attn_verify -- the packed multi-query verifier over INT8 pages: the
+ * last n_queries positions of each request attend causally in one pass over
+ * its pages (query i at position L - n_queries + i attends positions 0 ..
+ * L - n_queries + i; zeros if there is none).  q and out are
+ * [batch][n_queries][n_q_heads][256]; n_queries * (n_q_heads / n_kv_heads) <=
+ * TQ4_MAX_VERIFY_ROWS; n_queries == 1 is tq4_int8_attn_decode.  Other
+ * arguments as tq4_attn_verify. */
+tq4_status tq4_int8_attn_verify(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,
+                                const int32_t *page_table, int32_t page_table_stride,
+                                const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                int32_t n_q_heads, float scale, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /*
  * Host page allocator ([ST]: admission reserves page equivalents, shared
  * prefixes are reference counted, and a departing request gives its pages back

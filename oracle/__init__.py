@@ -454,28 +454,50 @@ def int8_encode_to_pool(pool: Int8Pool, k_src, v_src, slots) -> None:
             raise ValueError("slot outside the pool")
 
 
-def int8_attn_decode(pool: Int8Pool, q, page_table, seq_lens, scale: float, heads=None) -> np.ndarray:
-    """fp64 single-query decode attention over INT8 pages: q[b] attends positions 0..seq_lens[b]-1
-    of its page-table row.  Returns [batch][n_q][256]; heads outside `heads` stay 0."""
+def int8_attention(pool: Int8Pool, q, page_table, row_table, row_len, scale: float, heads=None) -> np.ndarray:
+    """fp64 softmax attention over INT8 pages (the same contract as `attention`): query row r reads
+    table row row_table[r] and attends its first row_len[r] positions.  Returns [n_rows][n_q][256];
+    heads outside `heads` = (h0, h1) stay 0."""
     q = np.ascontiguousarray(q, dtype=np.float64)
-    batch, n_q, d = q.shape
+    n_rows, n_q, d = q.shape
     assert d == DIM and n_q % pool.n_kv == 0
     pt = np.ascontiguousarray(page_table, dtype=np.int32)
     if pt.ndim == 1:
         pt = pt[None, :]
-    rows = np.arange(batch, dtype=np.int32)
-    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    rt = np.ascontiguousarray(row_table, dtype=np.int32)
+    rl = np.ascontiguousarray(row_len, dtype=np.int32)
+    assert rt.shape == (n_rows,) and rl.shape == (n_rows,)
     h0, h1 = heads if heads is not None else (0, n_q)
-    out = np.zeros((batch, n_q, DIM), np.float64)
+    out = np.zeros((n_rows, n_q, DIM), np.float64)
     rc = _load().tq4o_int8_attention(
         _ptr(pool.k_codes, ctypes.c_int8), _ptr(pool.k_scales, ctypes.c_uint16),
         _ptr(pool.v_codes, ctypes.c_int8), _ptr(pool.v_scales, ctypes.c_uint16),
-        pool.num_pages, pool.n_kv, pool.page_size, _ptr(q, ctypes.c_double), n_q, batch,
-        _ptr(pt, ctypes.c_int32), pt.shape[1], _ptr(rows, ctypes.c_int32), _ptr(lens, ctypes.c_int32),
+        pool.num_pages, pool.n_kv, pool.page_size, _ptr(q, ctypes.c_double), n_q, n_rows,
+        _ptr(pt, ctypes.c_int32), pt.shape[1], _ptr(rt, ctypes.c_int32), _ptr(rl, ctypes.c_int32),
         float(scale), h0, h1, _ptr(out, ctypes.c_double))
     if rc != 0:
         raise ValueError(f"oracle INT8 attention failed ({rc})")
     return out
+
+
+def int8_attn_decode(pool: Int8Pool, q, page_table, seq_lens, scale: float, heads=None) -> np.ndarray:
+    """fp64 single-query decode attention over INT8 pages: q[b] attends positions 0..seq_lens[b]-1
+    of its page-table row.  Returns [batch][n_q][256]; heads outside `heads` stay 0."""
+    batch = np.shape(q)[0]
+    return int8_attention(pool, q, page_table, np.arange(batch, dtype=np.int32),
+                          np.asarray(seq_lens, np.int32), scale, heads)
+
+
+def int8_attn_verify(pool: Int8Pool, q, page_table, seq_lens, scale: float, heads=None) -> np.ndarray:
+    """The packed multi-query verifier's definition (as attn_verify) over INT8 pages: q is
+    [batch][k][n_q][256]; query i of request b attends positions 0 .. L_b - k + i."""
+    q = np.asarray(q)
+    batch, k = q.shape[0], q.shape[1]
+    L = np.asarray(seq_lens, np.int64)
+    rows = np.repeat(np.arange(batch, dtype=np.int32), k)
+    lens = np.maximum(L[:, None] - k + np.arange(k)[None, :] + 1, 0).reshape(-1).astype(np.int32)
+    out = int8_attention(pool, q.reshape(batch * k, q.shape[2], DIM), page_table, rows, lens, scale, heads)
+    return out.reshape(q.shape)
 
 
 def int8_bytes_per_position(n_layers: int = 16, n_kv: int = 4) -> int:

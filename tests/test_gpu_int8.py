@@ -174,3 +174,45 @@ def test_encode_then_decode_round_trip():
     got = _decode(dpool, q_t, table, w.seq_lens, 1500)
     ref = oracle.int8_attn_decode(pool, q64, table, w.seq_lens, synth.SCALE)
     parity(got, ref, "int8 gpu-encoded")
+
+
+def _verify(dpool, q_t, table, lens, max_seq, workspace=None):
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    out = tq4.tq4_int8_attn_verify(dpool, q_t.cuda(), torch.from_numpy(np.ascontiguousarray(table, np.int32)).cuda(),
+                                   torch.tensor(lens, dtype=torch.int32).cuda(), max_seq, synth.SCALE,
+                                   workspace=workspace)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+# k x G rows: one, two and three 16-column blocks
+@pytest.mark.parametrize("k,n_q,n_kv", [(2, 24, 4), (4, 24, 4), (8, 24, 4), (3, 64, 4), (8, 4, 4), (5, 24, 4)])
+def test_verify_matches_oracle(k, n_q, n_kv):
+    w = synth.Workload(144, "i8v", "decode", 1, 64, 120, seq_lens=(3000, 700, 5), n_q=n_q, n_kv=n_kv)
+    pool, table = oracle_int8_pool(w)
+    q_t, q64 = bf16_queries(w, 0, w.batch * k)
+    q_t = q_t.reshape(w.batch, k, n_q, 256).contiguous()
+    q64 = q64.reshape(w.batch, k, n_q, 256)
+    ref = oracle.int8_attn_verify(pool, q64, table, w.seq_lens, synth.SCALE)
+    got = _verify(int8_to_device(pool), q_t, table, w.seq_lens, 3000)
+    parity(got, ref, f"int8 verify k={k} G={n_q // n_kv}")
+    for b, L in enumerate(w.seq_lens):
+        for i in range(k):
+            if L - k + i + 1 <= 0:
+                assert np.all(got[b, i].float().numpy() == 0.0)
+
+
+def test_verify_one_query_is_decode_bit_for_bit_and_garbage_tail():
+    import torch
+    w = synth.Workload(145, "i8v1", "decode", 1, 64, 160, seq_lens=(5000, 333, 64))
+    pool, table = oracle_int8_pool(w, fill=np.random.default_rng(9))
+    dpool = int8_to_device(pool)
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    one = _verify(dpool, q_t.reshape(w.batch, 1, w.n_q, 256).contiguous(), table, w.seq_lens, 5000)
+    dec = _decode(dpool, q_t, table, w.seq_lens, 5000)
+    assert torch.equal(one[:, 0], dec)
+    q4, q4_64 = bf16_queries(w, 1, w.batch * 4)
+    got = _verify(dpool, q4.reshape(w.batch, 4, w.n_q, 256).contiguous(), table, w.seq_lens, 5000)
+    parity(got, oracle.int8_attn_verify(pool, q4_64.reshape(w.batch, 4, w.n_q, 256), table, w.seq_lens,
+                                        synth.SCALE), "int8 verify garbage tail")

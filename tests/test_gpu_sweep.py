@@ -61,6 +61,10 @@ def test_sweep_decode_verify_int8(i):
     out8 = tq4.tq4_int8_attn_decode(int8_to_device(pool8), q_t.cuda(), tab, seq, max_seq, synth.SCALE)
     torch.cuda.synchronize()
     parity(out8.cpu(), oracle.int8_attn_decode(pool8, q64, table, w.seq_lens, synth.SCALE), "int8 " + what)
+    outv8 = tq4.tq4_int8_attn_verify(int8_to_device(pool8), qv.cuda(), tab, seq, max_seq, synth.SCALE)
+    torch.cuda.synchronize()
+    parity(outv8.cpu(), oracle.int8_attn_verify(pool8, qv64, table, w.seq_lens, synth.SCALE),
+           f"int8 verify k={k} " + what)
     # unfused chain against attention over the pages
     kd, vd = tq4.tq4_reconstruct_pages(dpool, tab, seq, max_seq)
     outs = tq4.tq4_sdpa_decode(q_t.cuda(), kd, vd, seq, synth.SCALE)

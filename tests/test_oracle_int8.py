@@ -244,3 +244,25 @@ def test_attention_equal_scores_is_mean_of_values(oracle_mod):
 def test_int8_bytes_per_position(oracle_mod):
     # 256 one-byte codes + a two-byte scale per vector, K and V, 4 KV heads, 16 layers
     assert oracle_mod.int8_bytes_per_position() == 16 * 4 * 2 * 258 == 33024
+
+
+def test_int8_verify_rows_are_decode_at_their_lengths(oracle_mod):
+    """Query i of k attends exactly the first L - k + i + 1 positions (each row equals a decode at
+    that length, bit for bit), and a query with no position gets zeros."""
+    rng = np.random.default_rng(49)
+    lens = (20, 2)
+    pool, table = _pool(oracle_mod, rng, 8, 2, 8, lens)
+    k = 4
+    q = rng.standard_normal((2, k, 4, DIM))
+    got = oracle_mod.int8_attn_verify(pool, q, table, lens, 0.0625)
+    for b, L in enumerate(lens):
+        for i in range(k):
+            n = L - k + i + 1
+            if n <= 0:
+                assert np.all(got[b, i] == 0.0)
+                continue
+            ref = oracle_mod.int8_attn_decode(pool, q[b, i][None], table[b:b + 1], [n], 0.0625)
+            np.testing.assert_array_equal(got[b, i], ref[0])
+            if n > 1:  # and differs from one position fewer
+                fewer = oracle_mod.int8_attn_decode(pool, q[b, i][None], table[b:b + 1], [n - 1], 0.0625)
+                assert not np.array_equal(got[b, i], fewer[0])
