@@ -369,23 +369,29 @@ def int8_leg(name: str, device, reps: int = 20) -> dict:
             "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
 
 
-def prefill_leg(device, reps: int = 3):
+def prefill_leg(device, reps: int = 3, int8: bool = False):
     """The chunked-prefill workload: 2,048 bf16 query tokens x 24 heads over 194,560 cached
-    positions plus the chunk itself (causal inside the chunk), one layer.  Reports the call
-    time and useful matrix-core throughput (4 * heads * 256 * attended pairs)."""
+    positions plus the chunk itself (causal inside the chunk), one layer, over TQ4 pages (or the
+    INT8 arm's pages).  Reports the call time and useful matrix-core throughput
+    (4 * heads * 256 * attended pairs)."""
     import torch
     import compressed_kv_attention_kvexec_amd as tq4
     import synth
     w = synth.WORKLOADS["prefill_2k_over_194k"]
     table = synth.placement(w, 0)
     slots = synth.used_slots(w, table)
-    pool = tq4.Tq4LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+    if int8:
+        pool = tq4.Int8LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+        encode = tq4.tq4_int8_encode_pages
+    else:
+        pool = tq4.Tq4LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=device)
+        encode = tq4.tq4_encode_pages
     sd = torch.from_numpy(slots).to(device)
     for which, st in ((0, synth.T_K), (1, synth.T_V)):
         src = synth.torch_normal(synth.seed_of(w.wid, 0, st), (len(slots), w.n_kv, 256), device)
         for c in range(0, len(slots), 65536):
             kv = (src[c:c + 65536], None) if which == 0 else (None, src[c:c + 65536])
-            tq4.tq4_encode_pages(pool, *kv, sd[c:c + 65536])
+            encode(pool, *kv, sd[c:c + 65536])
         del src
     q = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_Q), (w.chunk_len, w.n_q, 256), device)
     q = q.to(torch.bfloat16).contiguous()
@@ -393,7 +399,8 @@ def prefill_leg(device, reps: int = 3):
     ws = tq4.new_workspace(tq4.tq4_attn_prefill_workspace_size(w.prior_len, w.chunk_len, w.n_q, w.n_kv,
                                                                w.page_size), device)
     out = torch.empty_like(q)
-    call = tq4.prepare_prefill(pool, q, tb, w.prior_len, synth.SCALE, out, ws)
+    prepare = tq4.prepare_int8_prefill if int8 else tq4.prepare_prefill
+    call = prepare(pool, q, tb, w.prior_len, synth.SCALE, out, ws)
     call()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -724,6 +731,10 @@ def main() -> int:
         result["extra"]["prefill"] = prefill_leg(dev)
         log(f"prefill: {result['extra']['prefill']['ms_per_call']:.3f} ms/call, "
             f"{result['extra']['prefill']['achieved_tflops']:.1f} TFLOP/s")
+        if not args.no_int8:
+            r = prefill_leg(dev, int8=True)
+            result["extra"]["int8"]["prefill"] = r
+            log(f"int8 prefill: {r['ms_per_call']:.3f} ms/call, {r['achieved_tflops']:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_positions} positions ...")
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample_positions)

@@ -29,7 +29,8 @@ __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_e
            "tq4_sdpa_decode", "prepare_reconstruct", "prepare_sdpa_decode", "Int8LayerPool",
            "tq4_int8_encode_pages", "tq4_int8_attn_decode_workspace_size", "tq4_int8_attn_decode",
            "prepare_int8_decode", "tq4_int8_attn_verify_workspace_size", "tq4_int8_attn_verify",
-           "prepare_int8_verify"]
+           "prepare_int8_verify", "tq4_int8_attn_prefill_workspace_size", "tq4_int8_attn_prefill_chunk",
+           "prepare_int8_prefill"]
 
 HEAD_DIM = 256
 WORDS = 32
@@ -340,6 +341,26 @@ def tq4_int8_attn_verify(pool: Int8LayerPool, q: torch.Tensor, page_table: torch
     return out
 
 
+def tq4_int8_attn_prefill_workspace_size(prior_len: int, chunk_len: int, n_q_heads: int, n_kv_heads: int,
+                                         page_size: int) -> int:
+    return int(load_library().tq4_int8_attn_prefill_workspace_size(prior_len, chunk_len, n_q_heads,
+                                                                    n_kv_heads, page_size))
+
+
+def tq4_int8_attn_prefill_chunk(pool: Int8LayerPool, q: torch.Tensor, page_table: torch.Tensor, prior_len: int,
+                                scale: float, out: torch.Tensor | None = None,
+                                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q [chunk_len][n_q][256] bf16 over INT8 pages; page_table int32 covering prior_len + chunk_len positions."""
+    chunk_len, n_q, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_int8_attn_prefill_workspace_size(prior_len, chunk_len, n_q, pool.n_kv,
+                                                                       pool.page_size), q.device)
+    prepare_int8_prefill(pool, q, page_table, prior_len, scale, out, workspace, stream)()
+    return out
+
+
 class PreparedCall:
     """A library call with its ctypes arguments marshalled once.
 
@@ -449,3 +470,13 @@ def prepare_int8_verify(pool: Int8LayerPool, q: torch.Tensor, page_table: torch.
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     return PreparedCall(load_library().tq4_int8_attn_verify, args,
                         (ps, pool, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_int8_prefill(pool: Int8LayerPool, q: torch.Tensor, page_table: torch.Tensor, prior_len: int,
+                         scale: float, out: torch.Tensor, workspace: torch.Tensor, stream=None) -> PreparedCall:
+    chunk_len, n_q, _ = q.shape
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(prior_len), chunk_len, n_q,
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return PreparedCall(load_library().tq4_int8_attn_prefill_chunk, args, (ps, pool, q, page_table, out, workspace))

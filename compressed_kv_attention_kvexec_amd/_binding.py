@@ -96,6 +96,10 @@ def load_library(path: str | None = None):
     lib.tq4_int8_attn_verify_workspace_size.restype = sz
     lib.tq4_int8_attn_verify.argtypes = [i8p, vp, st, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
     lib.tq4_int8_attn_verify.restype = st
+    lib.tq4_int8_attn_prefill_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.tq4_int8_attn_prefill_workspace_size.restype = sz
+    lib.tq4_int8_attn_prefill_chunk.argtypes = [i8p, vp, st, vp, i32, i32, i32, f32, vp, vp, sz, vp]
+    lib.tq4_int8_attn_prefill_chunk.restype = st
     pp = ctypes.c_void_p
     i64 = ctypes.c_int64
     lib.tq4_pages_create.argtypes = [i32, i32, ctypes.POINTER(pp)]

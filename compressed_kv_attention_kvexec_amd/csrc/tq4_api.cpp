@@ -443,4 +443,47 @@ tq4_status tq4_int8_attn_verify(const tq4_int8_pool *pool, const void *q, tq4_dt
                        n_q_heads, scale, out, workspace, workspace_bytes, stream);
 }
 
+size_t tq4_int8_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,
+                                            int32_t n_kv_heads, int32_t page_size) {
+    return tq4_attn_prefill_workspace_size(prior_len, chunk_len, n_q_heads, n_kv_heads, page_size);
+}
+
+tq4_status tq4_int8_attn_prefill_chunk(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype,
+                                       const int32_t *page_table, int32_t prior_len, int32_t chunk_len,
+                                       int32_t n_q_heads, float scale, void *out, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    tq4_status st = check_int8_pool(pool);
+    if (st != TQ4_OK) return st;
+    if (!pool->k_codes || !pool->v_codes || !pool->k_scales || !pool->v_scales) return TQ4_ERR_NULL;
+    if (!aligned(pool->k_codes, 16) || !aligned(pool->v_codes, 16)) return TQ4_ERR_ALIGN;
+    if (!aligned(pool->k_scales, 8) || !aligned(pool->v_scales, 8)) return TQ4_ERR_ALIGN;
+    if (!q || !page_table || !out) return TQ4_ERR_NULL;
+    if (q_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
+    if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
+    if (prior_len < 0 || chunk_len < 1) return TQ4_ERR_SHAPE;
+    if (int64_t{prior_len} + chunk_len > (int64_t{1} << 31) - 1) return TQ4_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4)) return TQ4_ERR_ALIGN;
+    const tq4::PrefillPlan plan = tq4::plan_prefill(prior_len, chunk_len, n_q_heads, pool->n_kv_heads);
+    if (plan.n_qblocks > 65535 || pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
+    if (workspace == nullptr || workspace_bytes < plan.workspace_bytes) return TQ4_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return TQ4_ERR_ALIGN;
+    tq4::Int8PrefillParams p{};
+    p.k_codes = pool->k_codes;
+    p.v_codes = pool->v_codes;
+    p.k_scales = pool->k_scales;
+    p.v_scales = pool->v_scales;
+    p.num_pages = pool->num_pages;
+    p.page_size = pool->page_size;
+    p.n_kv = pool->n_kv_heads;
+    p.q = static_cast<const uint16_t *>(q);
+    p.page_table = page_table;
+    p.prior_len = prior_len;
+    p.chunk_len = chunk_len;
+    p.n_q = n_q_heads;
+    p.scale = scale;
+    p.out = static_cast<uint16_t *>(out);
+    p.workspace = workspace;
+    return from_hip(tq4::launch_int8_prefill(p, plan, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -632,4 +632,317 @@ hipError_t launch_int8_decode(const Int8DecodeParams &p, const DecodePlan &plan,
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- chunked prefill
+//
+// Causal attention of a chunk of query tokens over INT8 pages: the TQ4 prefill's decomposition
+// (grid (key split, 128-row block, KV head), 8 wavefronts of 16 rows, a double-buffered LDS image
+// of each 32-key tile's fp16 MFMA operands that the wavefronts fill together, one barrier per
+// tile) with the byte conversion in place of the table, the natural domain (no rotation), value
+// operands pre-scaled (code * scale, one fp16 rounding) and key scales in the scores.  Three
+// kernels per call: query rows to fp16 operands with a power-of-two scale; attend; the shared
+// prefill combine without the inverse rotation.
+
+constexpr int kI8PfWaves = 8;
+constexpr int kI8PfRowsPerWg = kI8PfWaves * 16;  // must equal the plan's rows per block
+constexpr int kI8PfAhead = 4;
+constexpr float kI8PfRescaleSlack = 8.0f;
+
+struct Int8PrefillArgs {
+    Int8PrefillParams p;
+    int32_t group;
+    int32_t rows;        // chunk_len * group (per KV head)
+    int32_t n_splits;
+    int32_t split_tiles;
+    uint64_t qop_off;    // fp16 [chunk_len * n_q][256], natural dim order
+    uint64_t frow_off;   // float [chunk_len * n_q]
+    uint64_t parts_off;  // float [n_kv][rows][n_splits][kPfPartial]
+};
+
+__global__ __launch_bounds__(256) void tq4_int8_prefill_query_kernel(Int8PrefillArgs a) {
+    const Int8PrefillParams &p = a.p;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // t * n_q + qh
+    if (row >= static_cast<int64_t>(p.chunk_len) * p.n_q) return;
+    const u32x2 raw = *reinterpret_cast<const u32x2 *>(p.q + row * kDim + 4 * lane);
+    const float y[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                        __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+    const int e = q_exponent(wave_max_abs(y));
+    const float qs = ldexpf(1.0f, e);
+    char *ws = static_cast<char *>(p.workspace);
+    u32x2 hv;
+    hv.x = pack_f16x2(y[0] * qs, y[1] * qs);
+    hv.y = pack_f16x2(y[2] * qs, y[3] * qs);
+    *reinterpret_cast<u32x2 *>(ws + a.qop_off + row * (kDim * 2) + 8 * lane) = hv;
+    if (lane == 0) reinterpret_cast<float *>(ws + a.frow_off)[row] = p.scale * 1.4426950408889634f * ldexpf(1.0f, -e);
+}
+
+// Tile image: entry mt * 8 + ks is the K operand of M-tile mt, K-step ks; entry 16 + e the
+// (pre-scaled) V operand of M-tile e; ksc the 32 key scales.
+struct I8PfTileImage {
+    half8 op[32][kWave];
+    float ksc[32];
+};
+
+__global__ __launch_bounds__(kI8PfWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void tq4_int8_prefill_kernel(Int8PrefillArgs a) {
+    constexpr int NW = kI8PfWaves;
+    __shared__ __align__(16) I8PfTileImage img[2];
+    const Int8PrefillParams &p = a.p;
+    const int G = a.group;
+    const int s = blockIdx.x, rb = blockIdx.y, g = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    char *ws = static_cast<char *>(p.workspace);
+
+    const int row0 = rb * kI8PfRowsPerWg + wave_u * 16;  // this wave's rows: row0 + n
+    const int wg_last_row = min(rb * kI8PfRowsPerWg + kI8PfRowsPerWg, a.rows) - 1;
+    const int wg_kmax = p.prior_len + wg_last_row / G + 1;  // keys any row of the workgroup sees
+    const int total_keys = p.prior_len + p.chunk_len;
+    const int split_keys = a.split_tiles * kTile;
+    const int key_begin = s * split_keys;
+    const int key_end = min(key_begin + split_keys, wg_kmax);
+    const int n_tiles = key_end > key_begin ? (key_end - key_begin + kTile - 1) / kTile : 0;
+
+    // ---- this wave's share of each tile: K operands e0, e0 + 1 and V operands 16 + e0, 16 + e0 + 1
+    // (e0 = 2 wave).  The K pair is bytes 64 (ks / 2) + 16 gq .. + 15 of key 16 mt + n (one 16-byte
+    // load; mt = e0 / 8, ks = e0 % 8).  The V pair takes bytes e0 and e0 + 1 of dims 16 n .. of keys
+    // sigma(0..7): one word per key (bytes 4 (e0 / 4) ..), shifted so the pair sits in bytes 0, 1.
+    const int e0 = 2 * wave_u;
+    const int mt_w = e0 >> 3, ks_w = e0 & 7;
+    const uint32_t k_lane_off = (16u * mt_w + n) * 256u + 64u * (ks_w >> 1) + 16u * gq;
+    const uint32_t v_lane_off = gq * 1024u + n * 16u + 4u * (e0 >> 2);
+    const uint32_t v_shift = 8u * (e0 & 3);  // 0 or 16
+    const int32_t *pt = p.page_table;
+    const int pt_last = (total_keys - 1) / p.page_size;
+    struct Staging {
+        u32x4 k;
+        uint32_t v[8];
+        u32x2 vs[2];
+        uint32_t ks;
+        int key0;
+        bool valid;
+    };
+    auto load_share = [&](Staging &st, int t) {
+        const int key0 = key_begin + t * kTile;  // t is clamped by the caller to a tile of this split
+        const int pid = pt[min(key0 / p.page_size, pt_last)];
+        const int64_t rec = tile_rec0(p, g, key0, pid, st.valid);
+        st.key0 = key0;
+        const char *kb = reinterpret_cast<const char *>(p.k_codes) + rec * kDim;
+        const char *vb = reinterpret_cast<const char *>(p.v_codes) + rec * kDim;
+        st.k = *reinterpret_cast<const u32x4 *>(kb + k_lane_off);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t koff = (j < 4) ? 256u * j : 4096u + 256u * (j - 4);
+            st.v[j] = *reinterpret_cast<const uint32_t *>(vb + v_lane_off + koff);
+        }
+        const char *vsb = reinterpret_cast<const char *>(p.v_scales) + rec * 2 + gq * 8u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) st.vs[h] = *reinterpret_cast<const u32x2 *>(vsb + 32u * h);
+        st.ks = p.k_scales[rec + (lane & 31)];
+    };
+    auto decode_share = [&](const Staging &st, I8PfTileImage &im) {
+        // value scales of keys past the cached length (or on an invalid page) become 0: their
+        // records may hold any bits, and the value operand is shared by every row
+        const int lim_v = st.valid ? total_keys - st.key0 : 0;
+        u32x2 vs[2] = {st.vs[0], st.vs[1]};
+        if (!__all(lim_v >= kTile)) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k0 = 16 * h + 4 * gq;
+                vs[h].x &= (k0 < lim_v ? 0xffffu : 0u) | (k0 + 1 < lim_v ? 0xffff0000u : 0u);
+                vs[h].y &= (k0 + 2 < lim_v ? 0xffffu : 0u) | (k0 + 3 < lim_v ? 0xffff0000u : 0u);
+            }
+        }
+        u32x4 k0v, k1v;
+        k0v.x = i8x2_to_f16x2<0, 1>(st.k.x, st.k.x);
+        k0v.y = i8x2_to_f16x2<2, 3>(st.k.x, st.k.x);
+        k0v.z = i8x2_to_f16x2<0, 1>(st.k.y, st.k.y);
+        k0v.w = i8x2_to_f16x2<2, 3>(st.k.y, st.k.y);
+        k1v.x = i8x2_to_f16x2<0, 1>(st.k.z, st.k.z);
+        k1v.y = i8x2_to_f16x2<2, 3>(st.k.z, st.k.z);
+        k1v.z = i8x2_to_f16x2<0, 1>(st.k.w, st.k.w);
+        k1v.w = i8x2_to_f16x2<2, 3>(st.k.w, st.k.w);
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = st.v[j] >> v_shift;
+        u32x4 v0, v1;
+        v0.x = mul_f16x2(i8x2_to_f16x2<0, 0>(w[0], w[1]), vs[0].x);
+        v0.y = mul_f16x2(i8x2_to_f16x2<0, 0>(w[2], w[3]), vs[0].y);
+        v0.z = mul_f16x2(i8x2_to_f16x2<0, 0>(w[4], w[5]), vs[1].x);
+        v0.w = mul_f16x2(i8x2_to_f16x2<0, 0>(w[6], w[7]), vs[1].y);
+        v1.x = mul_f16x2(i8x2_to_f16x2<1, 1>(w[0], w[1]), vs[0].x);
+        v1.y = mul_f16x2(i8x2_to_f16x2<1, 1>(w[2], w[3]), vs[0].y);
+        v1.z = mul_f16x2(i8x2_to_f16x2<1, 1>(w[4], w[5]), vs[1].x);
+        v1.w = mul_f16x2(i8x2_to_f16x2<1, 1>(w[6], w[7]), vs[1].y);
+        im.op[e0][lane] = __builtin_bit_cast(half8, k0v);
+        im.op[e0 + 1][lane] = __builtin_bit_cast(half8, k1v);
+        im.op[16 + e0][lane] = __builtin_bit_cast(half8, v0);
+        im.op[16 + e0 + 1][lane] = __builtin_bit_cast(half8, v1);
+        if (lane < 32) im.ksc[lane] = f16_bits_to_f32(static_cast<uint16_t>(st.ks));  // every wave: same values
+    };
+
+    Staging sa, sb;
+    load_share(sa, 0);
+
+    // ---- row data: causal limit, score factor, query operand (rows past the chunk see no key and
+    // are never written).  K-step ks takes dims 64 (ks / 2) + 16 gq + 8 (ks % 2) .. + 7.
+    const int row = row0 + n;
+    const bool live = row < a.rows;
+    const int tq = live ? row / G : 0;
+    const int qrow = tq * p.n_q + g * G + (live ? row - tq * G : 0);
+    const int lim_row = live ? p.prior_len + tq + 1 : 0;
+    const float fcol = live ? reinterpret_cast<const float *>(ws + a.frow_off)[qrow] : 1.f;
+    half8 qop[8];
+    {
+        const char *qr = ws + a.qop_off + static_cast<int64_t>(qrow) * (kDim * 2);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            u32x4 v = *reinterpret_cast<const u32x4 *>(qr + 2 * (64 * (ks >> 1) + 16 * gq + 8 * (ks & 1)));
+            if (!live) v = u32x4{0u, 0u, 0u, 0u};
+            qop[ks] = __builtin_bit_cast(half8, v);
+        }
+    }
+    const int t_last = max(n_tiles - 1, 0);
+    decode_share(sa, img[0]);
+    bool valid0 = sa.valid, valid1 = false;
+    load_share(sb, min(1, t_last));
+    load_share(sa, min(2, t_last));
+    __syncthreads();
+
+    float4v oacc[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) oacc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    auto compute = [&](const I8PfTileImage &im, int t, bool valid) {
+        const int key0 = key_begin + t * kTile;
+        float4v sacc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+        half8 opb[kI8PfAhead + 1];
+#pragma unroll
+        for (int e = 0; e < kI8PfAhead; ++e) opb[e] = im.op[e][lane];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (e + kI8PfAhead < 16) opb[(e + kI8PfAhead) % (kI8PfAhead + 1)] = im.op[e + kI8PfAhead][lane];
+            sacc[e >> 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(opb[e % (kI8PfAhead + 1)], qop[e & 7], sacc[e >> 3], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int e = 0; e < kI8PfAhead; ++e) opb[e] = im.op[16 + e][lane];
+        // lane holds keys sigma(j): j < 4 -> 4 gq + j, else 16 + 4 gq + j - 4
+        const float4 k0s = *reinterpret_cast<const float4 *>(&im.ksc[4 * gq]);
+        const float4 k1s = *reinterpret_cast<const float4 *>(&im.ksc[16 + 4 * gq]);
+        const float ksc[8] = {k0s.x, k0s.y, k0s.z, k0s.w, k1s.x, k1s.y, k1s.z, k1s.w};
+        const int lim = valid ? min(key_end, lim_row) - key0 : 0;
+        float xs[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xs[q] = sacc[q >> 2][q & 3] * ksc[q];
+        if (!__all(lim >= kTile)) {  // masked in place, so the common path has no copies
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int koff = (q < 4) ? (4 * gq + q) : (16 + 4 * gq + (q - 4));
+                if (koff >= lim) xs[q] = -INFINITY;
+            }
+        }
+        float mx = xs[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) mx = fmaxf(mx, xs[q]);
+        float lo, hi;
+        lane_pair<16>(mx, lo, hi);
+        mx = fmaxf(lo, hi);
+        lane_pair<32>(mx, lo, hi);
+        mx = fmaxf(lo, hi) * fcol;
+        if (__any(mx > m_run + kI8PfRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                oacc[tt] *= alpha;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            m_run = m_new;
+        }
+        const float neg_m = -fmaxf(m_run, -FLT_MAX);
+        float pv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            pv[q] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[q], fcol, neg_m));
+            l_run += pv[q];
+        }
+        u32x4 pr;
+        pr.x = pack_f16x2(pv[0], pv[1]);
+        pr.y = pack_f16x2(pv[2], pv[3]);
+        pr.z = pack_f16x2(pv[4], pv[5]);
+        pr.w = pack_f16x2(pv[6], pv[7]);
+        const half8 pop = __builtin_bit_cast(half8, pr);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (e + kI8PfAhead < 16) opb[(e + kI8PfAhead) % (kI8PfAhead + 1)] = im.op[16 + e + kI8PfAhead][lane];
+            oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(opb[e % (kI8PfAhead + 1)], pop, oacc[e], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        decode_share(sb, img[1]);
+        valid1 = sb.valid;
+        load_share(sb, min(t + 3, t_last));
+        compute(img[0], t, valid0);
+        __syncthreads();
+        decode_share(sa, img[0]);
+        valid0 = sa.valid;
+        load_share(sa, min(t + 4, t_last));
+        compute(img[1], t + 1, valid1 && t + 1 < n_tiles);
+        __syncthreads();
+    }
+
+    // ---- partial: lane (gq, n) holds row n, dims 16 (4 gq + r) + e in oacc[e][r]
+    float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+    l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
+    if (!live) return;
+    float *dst = reinterpret_cast<float *>(ws + a.parts_off) +
+                 ((static_cast<int64_t>(g) * a.rows + row) * a.n_splits + s) * kPfPartial;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float *d = dst + 16 * (4 * gq + r);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+            *reinterpret_cast<float4 *>(d + 4 * e4) =
+                make_float4(oacc[4 * e4][r], oacc[4 * e4 + 1][r], oacc[4 * e4 + 2][r], oacc[4 * e4 + 3][r]);
+    }
+    if (gq == 0) {
+        dst[kDim] = m_run;
+        dst[kDim + 1] = l_tot;
+    }
+}
+
+hipError_t launch_int8_prefill(const Int8PrefillParams &p, const PrefillPlan &plan, hipStream_t stream) {
+    if (plan.q_tokens_per_block != kI8PfRowsPerWg) return hipErrorInvalidValue;
+    Int8PrefillArgs a;
+    a.p = p;
+    a.group = plan.group;
+    a.rows = p.chunk_len * plan.group;
+    a.n_splits = plan.n_splits;
+    a.split_tiles = plan.split_tiles;
+    const size_t qrows = static_cast<size_t>(p.chunk_len) * p.n_q;
+    a.qop_off = 0;
+    a.frow_off = ((qrows * kDim * 2 + 255) / 256) * 256;
+    a.parts_off = plan.counters_bytes;
+    const int64_t q_blocks = (static_cast<int64_t>(qrows) + 3) / 4;
+    if (q_blocks > 0x7fffffff || plan.n_qblocks > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(tq4_int8_prefill_query_kernel, dim3(static_cast<unsigned>(q_blocks)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(tq4_int8_prefill_kernel, dim3(plan.n_splits, plan.n_qblocks, p.n_kv), dim3(kI8PfWaves * kWave), 0,
+                       stream, a);
+    PrefillCombineArgs c;
+    c.parts = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + a.parts_off);
+    c.out = p.out;
+    c.rows = a.rows;
+    c.group = a.group;
+    c.n_splits = a.n_splits;
+    c.n_kv = p.n_kv;
+    c.n_q = p.n_q;
+    return launch_prefill_combine(c, false, stream);
+}
+
 }  // namespace tq4

@@ -216,4 +216,40 @@ struct PrefillParams {
 
 hipError_t launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream);
 
+constexpr int kPfPartial = 256 + 4;  // prefill split partial per (KV head, row, split): O[256], max, sum, pad
+
+// Merge of prefill split partials into bf16 rows (the TQ4 path with the inverse rotation, the INT8
+// arm without).  Row r of a KV head is chunk token r / group, head r % group of the group.
+struct PrefillCombineArgs {
+    const float *parts;  // [n_kv][rows][n_splits][kPfPartial]
+    uint16_t *out;       // bf16 [chunk_len][n_q][256]
+    int32_t rows;
+    int32_t group;
+    int32_t n_splits;
+    int32_t n_kv;
+    int32_t n_q;
+};
+hipError_t launch_prefill_combine(const PrefillCombineArgs &c, bool rotated, hipStream_t stream);
+
+struct Int8PrefillParams {
+    const int8_t *k_codes;
+    const int8_t *v_codes;
+    const uint16_t *k_scales;
+    const uint16_t *v_scales;
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t n_kv;
+    const uint16_t *q;  // bf16 [chunk][n_q][256]
+    const int32_t *page_table;
+    int32_t prior_len;
+    int32_t chunk_len;
+    int32_t n_q;
+    float scale;
+    uint16_t *out;
+    void *workspace;
+};
+
+// plan: plan_prefill(prior_len, chunk_len, n_q, n_kv) (same workspace layout as the TQ4 prefill)
+hipError_t launch_int8_prefill(const Int8PrefillParams &p, const PrefillPlan &plan, hipStream_t stream);
+
 }  // namespace tq4

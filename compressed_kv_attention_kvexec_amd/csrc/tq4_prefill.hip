@@ -24,7 +24,7 @@
 //      O^T = V^T P^T); online softmax per row with the causal limit; a partial
 //      (O, max, sum) per row and split goes to the workspace;
 //   3. combine: one wavefront per row: merges the splits, inverse rotation,
-//      bf16 output.
+//      bf16 output (the same kernel without the rotation serves the INT8 arm).
 #include <cfloat>
 #include <type_traits>
 
@@ -38,7 +38,6 @@ constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfBlocks = 1;                               // R: 16-row blocks per wavefront
 constexpr int kPfRowsPerWg = kPfWaves * kPfBlocks * 16;   // 128
-constexpr int kPfPartial = kDim + 4;                       // O[256], max, sum, pad
 constexpr int kPfTargetWgs = 768;                          // 3 x 256 compute units
 constexpr int kPfAhead = 4;  // operand reads in flight ahead of the MFMAs that use them
 constexpr float kPfRescaleSlack = 8.0f;  // log2 headroom before a running maximum is moved
@@ -391,15 +390,14 @@ void tq4_prefill_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------- 3. combine
 
-__global__ __launch_bounds__(256) void tq4_prefill_combine_kernel(PrefillArgs a) {
-    const PrefillParams &p = a.p;
+template <bool kRotated>
+__global__ __launch_bounds__(256) void tq4_prefill_combine_kernel(PrefillCombineArgs a) {
     const int G = a.group;
     const int lane = threadIdx.x & 63;
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // g * rows + row
-    if (idx >= static_cast<int64_t>(p.n_kv) * a.rows) return;
+    if (idx >= static_cast<int64_t>(a.n_kv) * a.rows) return;
     const int g = static_cast<int>(idx / a.rows), row = static_cast<int>(idx % a.rows);
-    const float *base = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + a.parts_off) +
-                        idx * a.n_splits * kPfPartial;
+    const float *base = a.parts + idx * a.n_splits * kPfPartial;
     float M = -INFINITY;
     for (int k = 0; k < a.n_splits; ++k) M = fmaxf(M, base[k * kPfPartial + kDim]);
     float y[4] = {0.f, 0.f, 0.f, 0.f};
@@ -416,13 +414,26 @@ __global__ __launch_bounds__(256) void tq4_prefill_combine_kernel(PrefillArgs a)
         y[2] += w * v.z;
         y[3] += w * v.w;
     }
-    wave_fwht(y, lane);
-    const float f = L > 0.f ? (1.0f / 256.0f) / L : 0.f;
+    float f = L > 0.f ? 1.0f / L : 0.f;
+    if constexpr (kRotated) {  // o = H O / (256 L)
+        wave_fwht(y, lane);
+        f *= 1.0f / 256.0f;
+    }
     const int t = row / G, qh = g * G + (row - t * G);
     u32x2 o;
     o.x = static_cast<uint32_t>(f32_to_bf16(y[0] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[1] * f)) << 16);
     o.y = static_cast<uint32_t>(f32_to_bf16(y[2] * f)) | (static_cast<uint32_t>(f32_to_bf16(y[3] * f)) << 16);
-    *reinterpret_cast<u32x2 *>(p.out + (static_cast<int64_t>(t) * p.n_q + qh) * kDim + 4 * lane) = o;
+    *reinterpret_cast<u32x2 *>(a.out + (static_cast<int64_t>(t) * a.n_q + qh) * kDim + 4 * lane) = o;
+}
+
+hipError_t launch_prefill_combine(const PrefillCombineArgs &c, bool rotated, hipStream_t stream) {
+    const int64_t blocks = (static_cast<int64_t>(c.n_kv) * c.rows + 3) / 4;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (rotated)
+        hipLaunchKernelGGL(tq4_prefill_combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, c);
+    else
+        hipLaunchKernelGGL(tq4_prefill_combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream) {
@@ -443,8 +454,15 @@ hipError_t launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipSt
     hipLaunchKernelGGL(tq4_prefill_rotate_kernel, dim3(static_cast<unsigned>(rot_blocks)), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((tq4_prefill_kernel<kPfBlocks, kPfWaves>), dim3(plan.n_splits, plan.n_qblocks, p.n_kv), dim3(kPfThreads),
                        0, stream, a);
-    hipLaunchKernelGGL(tq4_prefill_combine_kernel, dim3(static_cast<unsigned>(comb_blocks)), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    PrefillCombineArgs c;
+    c.parts = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + a.parts_off);
+    c.out = p.out;
+    c.rows = a.rows;
+    c.group = a.group;
+    c.n_splits = a.n_splits;
+    c.n_kv = p.n_kv;
+    c.n_q = p.n_q;
+    return launch_prefill_combine(c, true, stream);
 }
 
 }  // namespace tq4

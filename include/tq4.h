@@ -390,6 +390,21 @@ tq4_status tq4_int8_attn_verify(const tq4_int8_pool *pool, const void *q, tq4_dt
                                 int32_t n_q_heads, float scale, void *out, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* Workspace bytes tq4_int8_attn_prefill_chunk needs (as
+ * tq4_attn_prefill_workspace_size). */
+size_t tq4_int8_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,
+                                            int32_t n_kv_heads, int32_t page_size);
+
+/* tq4_int8_attn_prefill_chunk -- causal attention of a chunk of query tokens
+ * over INT8 pages: query t (absolute position prior_len + t) attends
+ * positions 0 .. prior_len + t, whose records (the chunk's own included) the
+ * caller has already encoded.  Arguments, limits and workspace rules as
+ * tq4_attn_prefill_chunk. */
+tq4_status tq4_int8_attn_prefill_chunk(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype,
+                                       const int32_t *page_table, int32_t prior_len, int32_t chunk_len,
+                                       int32_t n_q_heads, float scale, void *out, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /*
  * Host page allocator ([ST]: admission reserves page equivalents, shared
  * prefixes are reference counted, and a departing request gives its pages back

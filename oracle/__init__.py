@@ -500,6 +500,14 @@ def int8_attn_verify(pool: Int8Pool, q, page_table, seq_lens, scale: float, head
     return out.reshape(q.shape)
 
 
+def int8_attn_prefill_rows(pool: Int8Pool, q_rows, rows, page_table_row, prior_len: int, scale: float,
+                           heads=None) -> np.ndarray:
+    """Chunk rows t (absolute position prior_len + t) attend positions 0..prior_len + t over INT8 pages."""
+    rows = np.asarray(rows, np.int32)
+    return int8_attention(pool, q_rows, np.asarray(page_table_row, np.int32)[None, :],
+                          np.zeros(len(rows), np.int32), prior_len + rows + 1, scale, heads)
+
+
 def int8_bytes_per_position(n_layers: int = 16, n_kv: int = 4) -> int:
     """INT8 bytes one cached position occupies across all full-attention layers (K and V)."""
     return n_layers * n_kv * 2 * (DIM + 2)

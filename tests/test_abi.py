@@ -256,3 +256,24 @@ def test_missing_library_fails_loudly(tmp_path):
     ) % (str(__import__("pathlib").Path(__file__).resolve().parents[1]), str(tmp_path / "libtq4.so"))
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120).stdout.split()
     assert out == ["raised", "True", "False"], out
+
+
+def test_int8_prefill_validation(lib):
+    pf = lib.tq4_int8_attn_prefill_chunk
+    p = _i8pool()
+    need = lib.tq4_int8_attn_prefill_workspace_size(1000, 100, 24, 4, 64)
+    assert need == lib.tq4_attn_prefill_workspace_size(1000, 100, 24, 4, 64) > 0
+    args = lambda **kw: dict(dict(pool=ctypes.byref(p), q=FAKE, dt=B.TQ4_BF16, table=FAKE, prior=1000, chunk=100,
+                                  n_q=24, out=FAKE, ws=FAKE, ws_bytes=need), **kw)
+    call = lambda a: pf(a["pool"], a["q"], a["dt"], a["table"], a["prior"], a["chunk"], a["n_q"], 0.0625, a["out"],
+                        a["ws"], a["ws_bytes"], None)
+    assert call(args(pool=None)) == 1
+    assert call(args(q=None)) == 1
+    assert call(args(dt=B.TQ4_F32)) == 3
+    assert call(args(chunk=0)) == 2
+    assert call(args(prior=-1)) == 2
+    assert call(args(n_q=22)) == 2
+    assert call(args(ws=None)) == 5
+    assert call(args(ws_bytes=need - 1)) == 5
+    assert call(args(ws=FAKE + 64)) == 4
+    assert call(args(q=FAKE + 2)) == 4

@@ -216,3 +216,58 @@ def test_verify_one_query_is_decode_bit_for_bit_and_garbage_tail():
     got = _verify(dpool, q4.reshape(w.batch, 4, w.n_q, 256).contiguous(), table, w.seq_lens, 5000)
     parity(got, oracle.int8_attn_verify(pool, q4_64.reshape(w.batch, 4, w.n_q, 256), table, w.seq_lens,
                                         synth.SCALE), "int8 verify garbage tail")
+
+
+def _prefill(dpool, q_t, table_row, prior):
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    out = tq4.tq4_int8_attn_prefill_chunk(dpool, q_t.cuda(), torch.from_numpy(np.ascontiguousarray(table_row, np.int32)).cuda(),
+                                          prior, synth.SCALE)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("prior,chunk,page,n_q,n_kv", [
+    (100, 28, 64, 24, 4),      # ragged pages, chunk inside one page
+    (0, 1, 64, 24, 4),         # a single token, nothing cached
+    (0, 77, 32, 6, 1),         # causal only
+    (3000, 300, 256, 24, 4),   # several row blocks and key splits
+    (1000, 130, 128, 64, 4),   # group of 16
+])
+def test_prefill_matches_oracle(prior, chunk, page, n_q, n_kv):
+    w = synth.Workload(146, "i8pf", "prefill", 1, page, (prior + chunk) // page + 5, prior_len=prior,
+                       chunk_len=chunk, n_q=n_q, n_kv=n_kv)
+    pool, table = oracle_int8_pool(w)
+    q_t, q64 = bf16_queries(w, 0, chunk)
+    ref = oracle.int8_attn_prefill_rows(pool, q64, np.arange(chunk), table[0], prior, synth.SCALE)
+    got = _prefill(int8_to_device(pool), q_t, table[0], prior)
+    parity(got, ref, f"int8 prefill prior={prior} chunk={chunk}")
+
+
+def test_prefill_garbage_tail_and_rows_equal_decode():
+    import torch
+    prior, chunk = 700, 40
+    w = synth.Workload(147, "i8pfg", "prefill", 1, 64, 20, prior_len=prior, chunk_len=chunk)
+    pool, table = oracle_int8_pool(w, fill=np.random.default_rng(10))
+    dpool = int8_to_device(pool)
+    q_t, q64 = bf16_queries(w, 0, chunk)
+    got = _prefill(dpool, q_t, table[0], prior)
+    parity(got, oracle.int8_attn_prefill_rows(pool, q64, np.arange(chunk), table[0], prior, synth.SCALE),
+           "int8 prefill garbage tail")
+    for t in (0, 17, 39):
+        dec = _decode(dpool, q_t[t:t + 1], table, [prior + t + 1], prior + t + 1)
+        assert (dec[0].double() - got[t].double()).abs().max().item() < 4e-3
+
+
+def test_prefill_full_size_sampled_rows():
+    """The 2,048-token chunk over 194,560 cached positions in its full launch; the oracle checks
+    sampled rows (first, last and between) of every head."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    w = synth.WORKLOADS["prefill_2k_over_194k"]
+    pool, table = oracle_int8_pool(w)
+    q_t, q64 = bf16_queries(w, 0, w.chunk_len)
+    got = _prefill(int8_to_device(pool), q_t, table[0], w.prior_len)
+    rows = np.array([0, 1, 1023, 2047])
+    ref = oracle.int8_attn_prefill_rows(pool, q64[rows], rows, table[0], w.prior_len, synth.SCALE)
+    parity(got[rows], ref, "int8 prefill 2k over 194k (sampled rows)")

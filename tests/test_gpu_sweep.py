@@ -89,4 +89,11 @@ def test_sweep_prefill(i):
                                      synth.SCALE)
     torch.cuda.synchronize()
     ref = oracle.attn_prefill_rows(pool, q64, np.arange(chunk), table[0], prior, synth.SCALE)
-    parity(out.cpu(), ref, f"prefill case {i}: page {page}, n_q {n_q}, n_kv {n_kv}, prior {prior}, chunk {chunk}")
+    what = f"case {i}: page {page}, n_q {n_q}, n_kv {n_kv}, prior {prior}, chunk {chunk}"
+    parity(out.cpu(), ref, "prefill " + what)
+    pool8, _ = oracle_int8_pool(w, table=table)
+    out8 = tq4.tq4_int8_attn_prefill_chunk(int8_to_device(pool8), q_t.cuda(), torch.from_numpy(table[0]).cuda(),
+                                           prior, synth.SCALE)
+    torch.cuda.synchronize()
+    parity(out8.cpu(), oracle.int8_attn_prefill_rows(pool8, q64, np.arange(chunk), table[0], prior, synth.SCALE),
+           "int8 prefill " + what)
