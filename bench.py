@@ -322,6 +322,25 @@ def int8_leg(name: str, device, reps: int = 20) -> dict:
     pages = sum(-(-L // w.page_size) for L in w.seq_lens)
     positions = sum(w.seq_lens)
     nbytes = positions * INT8_BYTES_PER_POS_LAYER + w.batch * w.n_q * 256 * 2 * 2 + pages * 4 + w.batch * 4
+    # the same call with the fused append: the new token's fp32 K and V written as the records of
+    # position seq_len - 1 of each request inside the launch
+    new_kv = synth.torch_normal(synth.seed_of(w.wid, 2, synth.T_K), (2, w.batch, w.n_kv, 256), device)
+    last = torch.tensor([int(table[b, (L - 1) // w.page_size]) * w.page_size + (L - 1) % w.page_size
+                         for b, L in enumerate(w.seq_lens)], dtype=torch.int32, device=device)
+    acall = tq4.prepare_int8_decode_append(pool, new_kv[0], new_kv[1], last, q, tab, seq, max(w.seq_lens),
+                                           synth.SCALE, out, ws)
+    for _ in range(2):
+        acall()
+    at = []
+    for _ in range(reps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        acall()
+        e1.record()
+        torch.cuda.synchronize()
+        at.append(e0.elapsed_time(e1) / 1e3)
+    t_append = sorted(at)[reps // 2]
     # the packed verifier over the same INT8 pages: the last k positions of each request
     verify = []
     for k in (2, 4, 8):
@@ -365,6 +384,7 @@ def int8_leg(name: str, device, reps: int = 20) -> dict:
             "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
             "int8_bytes_per_position_layer": INT8_BYTES_PER_POS_LAYER,
             "encode_vectors_per_s": tokens * w.n_kv * 2 / te, "encode_gb_per_s": enc_bytes / te / 1e9,
+            "append_us_per_call": t_append * 1e6,
             "verify": verify,
             "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
 

@@ -27,7 +27,7 @@ __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_e
            "tq4_attn_decode_append", "prepare_decode_append", "tq4_attn_verify_workspace_size",
            "tq4_attn_verify", "prepare_verify", "tq4_reconstruct_pages", "tq4_sdpa_decode_workspace_size",
            "tq4_sdpa_decode", "prepare_reconstruct", "prepare_sdpa_decode", "Int8LayerPool",
-           "tq4_int8_encode_pages", "tq4_int8_attn_decode_workspace_size", "tq4_int8_attn_decode",
+           "tq4_int8_encode_pages", "tq4_int8_attn_decode_workspace_size", "tq4_int8_attn_decode", "tq4_int8_attn_decode_append", "prepare_int8_decode_append",
            "prepare_int8_decode", "tq4_int8_attn_verify_workspace_size", "tq4_int8_attn_verify",
            "prepare_int8_verify", "tq4_int8_attn_prefill_workspace_size", "tq4_int8_attn_prefill_chunk",
            "prepare_int8_prefill"]
@@ -321,6 +321,23 @@ def tq4_int8_attn_decode(pool: Int8LayerPool, q: torch.Tensor, page_table: torch
     return out
 
 
+def tq4_int8_attn_decode_append(pool: Int8LayerPool, k_new, v_new, new_slots: torch.Tensor, q: torch.Tensor,
+                                page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                stream=None) -> torch.Tensor:
+    """INT8 pages: encode each request's new token (k_new / v_new [batch][n_kv][256] fp32 or bf16,
+    written at new_slots[b], the slot of position seq_lens[b] - 1) and attend, in one call."""
+    batch, n_q, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = new_workspace(tq4_int8_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                      pool.page_size), q.device)
+    prepare_int8_decode_append(pool, k_new, v_new, new_slots, q, page_table, seq_lens, max_seq_len, scale, out,
+                               workspace, stream)()
+    return out
+
+
 def tq4_int8_attn_verify_workspace_size(batch: int, max_seq_len: int, n_queries: int, n_q_heads: int,
                                         n_kv_heads: int, page_size: int) -> int:
     return int(load_library().tq4_int8_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q_heads,
@@ -458,6 +475,20 @@ def prepare_int8_decode(pool: Int8LayerPool, q: torch.Tensor, page_table: torch.
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     return PreparedCall(load_library().tq4_int8_attn_decode, args,
                         (ps, pool, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_int8_decode_append(pool: Int8LayerPool, k_new, v_new, new_slots: torch.Tensor, q: torch.Tensor,
+                               page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                               out: torch.Tensor, workspace: torch.Tensor, stream=None) -> PreparedCall:
+    batch, n_q, _ = q.shape
+    src = k_new if k_new is not None else v_new
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _dtype_code(src), _ptr(new_slots), _ptr(q), _dtype_code(q),
+            _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len), n_q,
+            ctypes.c_float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    return PreparedCall(load_library().tq4_int8_attn_decode_append, args,
+                        (ps, pool, k_new, v_new, new_slots, q, page_table, seq_lens, out, workspace))
 
 
 def prepare_int8_verify(pool: Int8LayerPool, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,

@@ -92,6 +92,9 @@ def load_library(path: str | None = None):
     lib.tq4_int8_attn_decode_workspace_size.restype = sz
     lib.tq4_int8_attn_decode.argtypes = [i8p, vp, st, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
     lib.tq4_int8_attn_decode.restype = st
+    lib.tq4_int8_attn_decode_append.argtypes = [i8p, vp, vp, st, vp, vp, st, vp, i32, vp, i32, i32, i32, f32, vp,
+                                                vp, sz, vp]
+    lib.tq4_int8_attn_decode_append.restype = st
     lib.tq4_int8_attn_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.tq4_int8_attn_verify_workspace_size.restype = sz
     lib.tq4_int8_attn_verify.argtypes = [i8p, vp, st, i32, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]

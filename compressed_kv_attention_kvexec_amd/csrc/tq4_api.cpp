@@ -379,7 +379,8 @@ size_t tq4_int8_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, i
 
 namespace {
 
-tq4_status int8_common(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,
+tq4_status int8_common(const tq4_int8_pool *pool, const void *k_new, const void *v_new, tq4_dtype src_dtype,
+                       const int32_t *new_slots, bool append, const void *q, tq4_dtype q_dtype, int32_t n_queries,
                        const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
                        int32_t batch, int32_t max_seq_len, int32_t n_q_heads, float scale, void *out,
                        void *workspace, size_t workspace_bytes, void *stream) {
@@ -398,6 +399,12 @@ tq4_status int8_common(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dty
         return TQ4_ERR_SHAPE;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
         return TQ4_ERR_ALIGN;
+    if (append) {
+        if ((k_new == nullptr && v_new == nullptr) || new_slots == nullptr) return TQ4_ERR_NULL;
+        if (src_dtype != TQ4_F32 && src_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
+        if ((k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)) || !aligned(new_slots, 4))
+            return TQ4_ERR_ALIGN;
+    }
     const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads, n_queries);
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return TQ4_ERR_WORKSPACE;
@@ -420,6 +427,12 @@ tq4_status int8_common(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dty
     p.scale = scale;
     p.out = static_cast<uint16_t *>(out);
     p.workspace = workspace;
+    if (append) {
+        p.k_new = k_new;
+        p.v_new = v_new;
+        p.new_bf16 = src_dtype == TQ4_BF16;
+        p.new_slots = new_slots;
+    }
     return from_hip(tq4::launch_int8_decode(p, plan, static_cast<hipStream_t>(stream)));
 }
 
@@ -430,8 +443,18 @@ tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dt
                                 const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                                 int32_t n_q_heads, float scale, void *out, void *workspace,
                                 size_t workspace_bytes, void *stream) {
-    return int8_common(pool, q, q_dtype, 1, page_table, page_table_stride, seq_lens, batch, max_seq_len,
-                       n_q_heads, scale, out, workspace, workspace_bytes, stream);
+    return int8_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, 1, page_table, page_table_stride,
+                       seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace, workspace_bytes, stream);
+}
+
+tq4_status tq4_int8_attn_decode_append(const tq4_int8_pool *pool, const void *k_new, const void *v_new,
+                                       tq4_dtype src_dtype, const int32_t *new_slots, const void *q,
+                                       tq4_dtype q_dtype, const int32_t *page_table, int32_t page_table_stride,
+                                       const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                       int32_t n_q_heads, float scale, void *out, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    return int8_common(pool, k_new, v_new, src_dtype, new_slots, true, q, q_dtype, 1, page_table, page_table_stride,
+                       seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace, workspace_bytes, stream);
 }
 
 tq4_status tq4_int8_attn_verify(const tq4_int8_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,
@@ -439,8 +462,9 @@ tq4_status tq4_int8_attn_verify(const tq4_int8_pool *pool, const void *q, tq4_dt
                                 const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
                                 int32_t n_q_heads, float scale, void *out, void *workspace,
                                 size_t workspace_bytes, void *stream) {
-    return int8_common(pool, q, q_dtype, n_queries, page_table, page_table_stride, seq_lens, batch, max_seq_len,
-                       n_q_heads, scale, out, workspace, workspace_bytes, stream);
+    return int8_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, n_queries, page_table,
+                       page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t tq4_int8_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int32_t n_q_heads,

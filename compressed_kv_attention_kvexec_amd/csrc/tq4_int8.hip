@@ -60,6 +60,15 @@ __device__ __forceinline__ uint32_t int8_code(float x, float s) {
     return static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu;
 }
 
+// One vector held by a wavefront (lane l: dims 4 l .. 4 l + 3): returns the lane's four codes as
+// one word (dim 4 l in the low byte) and sets the record's scale (fp16 bits).
+__device__ __forceinline__ uint32_t int8_encode_lane(const float x[4], uint16_t &s16) {
+    s16 = f32_to_f16_bits(wave_max_abs(x) / 127.0f);
+    const float s = f16_bits_to_f32(s16);
+    if (!(s > 0.0f)) return 0u;
+    return int8_code(x[0], s) | (int8_code(x[1], s) << 8) | (int8_code(x[2], s) << 16) | (int8_code(x[3], s) << 24);
+}
+
 // Each wavefront encodes vectors wave0, wave0 + stride, ... ([half][token][kv head] order); lane l
 // holds dims 4 l .. 4 l + 3 and stores their four codes as one word; lane 0 stores the scale.  The
 // next vector is requested before the current one is encoded; stores go through buffer resources
@@ -91,12 +100,8 @@ __global__ __launch_bounds__(kI8EncWaves * kWave) void tq4_int8_encode_kernel(In
         const int sl = valid ? s_u : 0;
         const int page = sl / a.p.page_size;
         const int64_t rec = (static_cast<int64_t>(page) * a.p.n_kv + head) * a.p.page_size + (sl - page * a.p.page_size);
-        const float amax = wave_max_abs(x);
-        const uint16_t s16 = f32_to_f16_bits(amax / 127.0f);
-        const float s = f16_bits_to_f32(s16);
-        uint32_t word = 0;
-        if (s > 0.0f)
-            word = int8_code(x[0], s) | (int8_code(x[1], s) << 8) | (int8_code(x[2], s) << 16) | (int8_code(x[3], s) << 24);
+        uint16_t s16;
+        const uint32_t word = int8_encode_lane(x, s16);
         const __amdgpu_buffer_rsrc_t cr =
             __builtin_amdgcn_make_buffer_rsrc(a.p.codes[half] + rec * kDim, 0, valid ? kDim : 0, kI8BufferFlags);
         const __amdgpu_buffer_rsrc_t sr =
@@ -283,6 +288,7 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_int8_split_kernel(Int8Dec
     const int split_keys = a.split_tiles * kTile;
     const int key_begin = s * split_keys;
     const int32_t *pt_row = p.page_table + static_cast<int64_t>(b) * p.table_stride;
+    const bool append_mode = p.k_new != nullptr || p.v_new != nullptr;
     // element offset of query row r (token i, head h) in q and out: [request][token][q head][256]
     auto row_off = [&](int r) -> int64_t {
         const int i = r / G, h = r - i * G;
@@ -364,6 +370,38 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_int8_split_kernel(Int8Dec
             zero_column(r);
     }
     __syncthreads();
+
+    // ---- append (decode only): the wavefront that owns the request's last tile is the only one
+    // that reads it, so it writes the new token's K and V records (position seq_len - 1) here,
+    // with the encoder's arithmetic, before its loop; if the first tile it requested above is that
+    // last tile, it requests the tile again once the stores are complete.
+    if constexpr (NB == 1) {
+        if (append_mode && s == n_active - 1 && n_tiles > 0 && slot == (n_tiles - 1) % NS) {
+            const int slot_new = p.new_slots[b];
+            if (slot_new >= 0 && slot_new < p.num_pages * p.page_size) {
+                const int page = slot_new / p.page_size;
+                const int64_t rec =
+                    (static_cast<int64_t>(page) * p.n_kv + g) * p.page_size + (slot_new - page * p.page_size);
+                const size_t off = (static_cast<size_t>(b) * p.n_kv + g) * kDim * (p.new_bf16 ? 2 : 4);
+                float xk[4], xv[4];
+                if (p.k_new != nullptr) encode_load(static_cast<const char *>(p.k_new) + off, p.new_bf16 != 0, lane, xk);
+                if (p.v_new != nullptr) encode_load(static_cast<const char *>(p.v_new) + off, p.new_bf16 != 0, lane, xv);
+                auto put = [&](const float x[4], const int8_t *codes, const uint16_t *scales) {
+                    uint16_t s16;
+                    const uint32_t word = int8_encode_lane(x, s16);
+                    reinterpret_cast<uint32_t *>(const_cast<int8_t *>(codes) + rec * kDim)[lane] = word;
+                    if (lane == 0) const_cast<uint16_t *>(scales)[rec] = s16;
+                };
+                if (p.k_new != nullptr) put(xk, p.k_codes, p.k_scales);
+                if (p.v_new != nullptr) put(xv, p.v_codes, p.v_scales);
+            }
+            // vmcnt(0): the record stores (and the first tile) have completed before the
+            // wavefront loads the last tile (vmcnt bits [3:0] and [15:14] zero, expcnt and
+            // lgkmcnt left at max)
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            if (n_mine == 1) issue(slot, 0, true);
+        }
+    }
 
     // this lane's column r = 16 blk + n: score factor and causal limit (padding columns see every
     // key and are never written)

@@ -178,9 +178,15 @@ struct Int8DecodeParams {
     float scale;
     uint16_t *out;  // bf16 bits [batch][n_q][256]
     void *workspace;
+    // optional (decode only): encode one new token per request before attending (NULL k_new and
+    // v_new: none)
+    const void *k_new;  // [batch][n_kv][256] fp32 or bf16
+    const void *v_new;
+    int32_t new_bf16;
+    const int32_t *new_slots;  // [batch]
 };
 
-// plan: plan_decode(batch, max_seq_len, n_q, n_kv, 1)
+// plan: plan_decode(batch, max_seq_len, n_q, n_kv, n_queries)
 hipError_t launch_int8_decode(const Int8DecodeParams &p, const DecodePlan &plan, hipStream_t stream);
 
 struct PrefillPlan {

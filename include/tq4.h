@@ -373,6 +373,21 @@ tq4_status tq4_int8_attn_decode(const tq4_int8_pool *pool, const void *q, tq4_dt
                                 int32_t n_q_heads, float scale, void *out, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/* tq4_int8_attn_decode_append -- the INT8 decode step of a layer in one call:
+ * encode each request's new token (the encoding rule above) and attend.
+ * Results are bit-identical to tq4_int8_encode_pages(pool, k_new, v_new,
+ * src_dtype, new_slots, batch) followed by tq4_int8_attn_decode(...) with the
+ * other arguments, provided new_slots[b] is the slot of position
+ * seq_lens[b] - 1 of request b; argument rules, the skipping of slots outside
+ * the pool and of empty requests, and the race on a new slot that another
+ * position of the call reads, as tq4_attn_decode_append. */
+tq4_status tq4_int8_attn_decode_append(const tq4_int8_pool *pool, const void *k_new, const void *v_new,
+                                       tq4_dtype src_dtype, const int32_t *new_slots, const void *q,
+                                       tq4_dtype q_dtype, const int32_t *page_table, int32_t page_table_stride,
+                                       const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                       int32_t n_q_heads, float scale, void *out, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /* Workspace bytes tq4_int8_attn_verify needs (as tq4_attn_verify_workspace_size). */
 size_t tq4_int8_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, int32_t n_queries,
                                            int32_t n_q_heads, int32_t n_kv_heads, int32_t page_size);

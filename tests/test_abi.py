@@ -213,6 +213,30 @@ def test_int8_decode_validation(lib):
     assert _i8decode(lib, ws=FAKE + 128) == 4
 
 
+def _append(lib, fn, pool, k=FAKE, v=FAKE, src=B.TQ4_F32, slots=FAKE, q=FAKE, table=FAKE, seq=FAKE, batch=1,
+            max_seq=4000, ws_bytes=1 << 30):
+    return fn(ctypes.byref(pool), k, v, src, slots, q, B.TQ4_BF16, table, 64, seq, batch, max_seq, 24, 0.0625,
+              FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("which", ["tq4", "int8"])
+def test_decode_append_validation(lib, which):
+    fn = lib.tq4_attn_decode_append if which == "tq4" else lib.tq4_int8_attn_decode_append
+    pool = _pool() if which == "tq4" else _i8pool()
+    assert _append(lib, fn, pool, k=None, v=None) == 1       # nothing to append
+    assert _append(lib, fn, pool, slots=None) == 1
+    assert _append(lib, fn, pool, q=None) == 1
+    assert _append(lib, fn, pool, src=B.TQ4_F16) == 3          # sources: fp32 or bf16
+    assert _append(lib, fn, pool, k=FAKE + 4) == 4
+    assert _append(lib, fn, pool, v=FAKE + 8) == 4
+    assert _append(lib, fn, pool, slots=FAKE + 2) == 4
+    assert _append(lib, fn, pool, batch=0) == 2
+    assert _append(lib, fn, pool, max_seq=4097) == 2
+    assert _append(lib, fn, pool, ws_bytes=0) == 5
+    assert fn(None, FAKE, FAKE, B.TQ4_F32, FAKE, FAKE, B.TQ4_BF16, FAKE, 64, FAKE, 1, 4000, 24, 0.0625, FAKE,
+              FAKE, 1 << 30, None) == 1
+
+
 def test_int8_encode_validation(lib):
     enc = lib.tq4_int8_encode_pages
     p = _i8pool()

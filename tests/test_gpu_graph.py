@@ -58,8 +58,8 @@ def test_decode_append_step_graph_replays_match_eager():
 
 
 def test_other_entry_points_graph_replays_match_eager():
-    """Verify, prefill, the unfused pair and the INT8 encode + decode captured in one graph: every
-    replay equals the eager results bit for bit."""
+    """Verify, prefill, the unfused pair and the INT8 encode, decode and decode-with-append captured
+    in one graph: every replay equals the eager results bit for bit."""
     import torch
     import compressed_kv_attention_kvexec_amd as tq4
     from _pools import int8_to_device, oracle_int8_pool
@@ -84,6 +84,9 @@ def test_other_entry_points_graph_replays_match_eager():
     knew = torch.from_numpy(rng.standard_normal((3, w.n_kv, 256)).astype(np.float32)).cuda()
     new_slots = torch.tensor([int(table[1, 12]) * 64 + 5, int(table[1, 12]) * 64 + 6, int(table[1, 12]) * 64 + 7],
                              dtype=torch.int32).cuda()
+    kv_app = torch.from_numpy(rng.standard_normal((2, 2, w.n_kv, 256)).astype(np.float32)).to(torch.bfloat16).cuda()
+    app_slots = torch.tensor([int(table[b, (L - 1) // 64]) * 64 + (L - 1) % 64 for b, L in enumerate(w.seq_lens)],
+                             dtype=torch.int32).cuda()
 
     s = torch.cuda.Stream()
     ws_v = tq4.new_workspace(tq4.tq4_attn_verify_workspace_size(2, 2000, 4, 24, 4, 64))
@@ -94,6 +97,8 @@ def test_other_entry_points_graph_replays_match_eager():
     out_d = torch.empty_like(qd)
     out_p = torch.empty_like(qp)
     out_s = torch.empty_like(qd)
+    out_a = torch.empty_like(qd)
+    ws_a = tq4.new_workspace(tq4.tq4_int8_attn_decode_workspace_size(2, 2000, 24, 4, 64))
     k_dense = torch.zeros((2, w.n_kv, 2000, 256), dtype=torch.bfloat16, device="cuda")
     v_dense = torch.zeros_like(k_dense)
     calls = [
@@ -105,6 +110,9 @@ def test_other_entry_points_graph_replays_match_eager():
 
     def int8_calls():
         tq4.tq4_int8_encode_pages(dpool8, knew, knew, new_slots, stream=s)
+        # the append first: it rewrites the last records the same way on every replay
+        tq4.tq4_int8_attn_decode_append(dpool8, kv_app[0], kv_app[1], app_slots, qd, tab, seq, 2000, synth.SCALE,
+                                        out=out_a, workspace=ws_a, stream=s)
         tq4.tq4_int8_attn_decode(dpool8, qd, tab, seq, 2000, synth.SCALE, out=out_d, workspace=ws_d, stream=s)
 
     s.wait_stream(torch.cuda.current_stream())
@@ -113,7 +121,7 @@ def test_other_entry_points_graph_replays_match_eager():
             c()
         int8_calls()
     torch.cuda.synchronize()
-    ref = [o.clone() for o in (out_v, out_p, out_s, out_d)]
+    ref = [o.clone() for o in (out_v, out_p, out_s, out_d, out_a)]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for c in calls:
@@ -121,12 +129,13 @@ def test_other_entry_points_graph_replays_match_eager():
         int8_calls()
     x = torch.randn(512, 512, device="cuda")
     for rep in range(4):
-        for o in (out_v, out_p, out_s, out_d):
+        for o in (out_v, out_p, out_s, out_d, out_a):
             o.fill_(0)
         y = x @ x
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, o, r in zip(("verify", "prefill", "sdpa", "int8"), (out_v, out_p, out_s, out_d), ref):
+        for name, o, r in zip(("verify", "prefill", "sdpa", "int8", "int8 append"),
+                              (out_v, out_p, out_s, out_d, out_a), ref):
             assert torch.equal(o, r), f"replay {rep}: {name}"
         assert torch.isfinite(y).all()

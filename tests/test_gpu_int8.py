@@ -271,3 +271,76 @@ def test_prefill_full_size_sampled_rows():
     rows = np.array([0, 1, 1023, 2047])
     ref = oracle.int8_attn_prefill_rows(pool, q64[rows], rows, table[0], w.prior_len, synth.SCALE)
     parity(got[rows], ref, "int8 prefill 2k over 194k (sampled rows)")
+
+
+def _append_case(seed, lens, page=64):
+    w = synth.Workload(seed, "i8append", "decode", 1, page, sum(-(-L // page) for L in lens) + 8, seq_lens=lens)
+    pool, table = oracle_int8_pool(w)
+    rng = np.random.default_rng(seed)
+    # K spans magnitudes (a peaked softmax on the new token); V stays at the workload's unit scale,
+    # where the absolute output bound is meaningful for bf16 outputs
+    new = rng.standard_normal((2, w.batch, w.n_kv, 256))
+    new[0] *= rng.uniform(0.01, 30.0, (w.batch, w.n_kv, 1))
+    last = np.array([table[b, (L - 1) // page] * page + (L - 1) % page for b, L in enumerate(lens)], np.int32)
+    return w, pool, table, new.astype(np.float32), last
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_append_equals_encode_then_decode(dtype):
+    """The fused INT8 append writes the records tq4_int8_encode_pages writes (and the oracle's
+    encoder), and returns the bits tq4_int8_attn_decode returns on the updated pool; a second call
+    reuses the workspace; the result meets the oracle's attention on the updated records."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    lens = (1, 31, 32, 33, 63, 64, 65, 2000, 777)
+    w, pool, table, new, last = _append_case(180, lens)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    k_new, v_new = (torch.from_numpy(new[i]).to(tdt).cuda().contiguous() for i in range(2))
+    slots = torch.from_numpy(last).cuda()
+    tab = torch.from_numpy(table).cuda()
+    seq = torch.tensor(lens, dtype=torch.int32).cuda()
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    ref_pool = int8_to_device(pool)
+    tq4.tq4_int8_encode_pages(ref_pool, k_new, v_new, slots)
+    ref = tq4.tq4_int8_attn_decode(ref_pool, q_t.cuda(), tab, seq, max(lens), synth.SCALE)
+    fused_pool = int8_to_device(pool)
+    ws = tq4.new_workspace(tq4.tq4_int8_attn_decode_workspace_size(w.batch, max(lens), w.n_q, w.n_kv, 64))
+    for _ in range(2):
+        got = tq4.tq4_int8_attn_decode_append(fused_pool, k_new, v_new, slots, q_t.cuda(), tab, seq, max(lens),
+                                              synth.SCALE, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+    for a, b in zip(_host(fused_pool), _host(ref_pool)):
+        np.testing.assert_array_equal(a, b)
+    chk = oracle.Int8Pool(*(x.copy() for x in (pool.k_codes, pool.k_scales, pool.v_codes, pool.v_scales)))
+    oracle.int8_encode_to_pool(chk, np.asarray(k_new.float().cpu()), np.asarray(v_new.float().cpu()), last)
+    got_h = _host(fused_pool)
+    for a, b in zip(got_h, (chk.k_codes, chk.k_scales, chk.v_codes, chk.v_scales)):
+        np.testing.assert_array_equal(a, b)
+    parity(got.cpu(), oracle.int8_attn_decode(chk, q64, table, lens, synth.SCALE), "int8 append")
+
+
+def test_decode_append_one_half_and_skipped_slots():
+    """k_new alone leaves the V records as they were; a slot outside the pool writes nothing; an
+    empty request writes nothing and returns zeros."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    lens = (500, 129, 0)
+    w, pool, table, new, last = _append_case(181, lens)
+    last[1] = -1
+    last[2] = 7  # a valid slot, but the request is empty: nothing is written
+    k_new = torch.from_numpy(new[0]).cuda()
+    tab = torch.from_numpy(table).cuda()
+    seq = torch.tensor(lens, dtype=torch.int32).cuda()
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    dpool = int8_to_device(pool)
+    got = tq4.tq4_int8_attn_decode_append(dpool, k_new, None, torch.from_numpy(last).cuda(), q_t.cuda(), tab,
+                                          seq, max(lens), synth.SCALE)
+    torch.cuda.synchronize()
+    chk = oracle.Int8Pool(*(x.copy() for x in (pool.k_codes, pool.k_scales, pool.v_codes, pool.v_scales)))
+    oracle.int8_encode_to_pool(chk, new[0][:1], None, last[:1])
+    for a, b in zip(_host(dpool), (chk.k_codes, chk.k_scales, chk.v_codes, chk.v_scales)):
+        np.testing.assert_array_equal(a, b)
+    ref = oracle.int8_attn_decode(chk, q64, table, lens, synth.SCALE)
+    parity(got.cpu(), ref, "int8 append, K only")
+    assert not got[2].any()
