@@ -922,16 +922,33 @@ void tq4_int8_prefill_kernel(Int8PrefillArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // the two wavefronts of a SIMD take each step's halves in opposite orders, as in the TQ4
+    // prefill (the barrier only separates the two image buffers)
+    const bool late = wave_u >= kI8PfWaves / 2;
     for (int t = 0; t < n_tiles; t += 2) {
-        decode_share(sb, img[1]);
-        valid1 = sb.valid;
-        load_share(sb, min(t + 3, t_last));
+        if (!late) {
+            decode_share(sb, img[1]);
+            valid1 = sb.valid;
+            load_share(sb, min(t + 3, t_last));
+        }
         compute(img[0], t, valid0);
+        if (late) {
+            decode_share(sb, img[1]);
+            valid1 = sb.valid;
+            load_share(sb, min(t + 3, t_last));
+        }
         __syncthreads();
-        decode_share(sa, img[0]);
-        valid0 = sa.valid;
-        load_share(sa, min(t + 4, t_last));
+        if (!late) {
+            decode_share(sa, img[0]);
+            valid0 = sa.valid;
+            load_share(sa, min(t + 4, t_last));
+        }
         compute(img[1], t + 1, valid1 && t + 1 < n_tiles);
+        if (late) {
+            decode_share(sa, img[0]);
+            valid0 = sa.valid;
+            load_share(sa, min(t + 4, t_last));
+        }
         __syncthreads();
     }
 

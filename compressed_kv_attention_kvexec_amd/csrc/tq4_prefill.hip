@@ -353,16 +353,35 @@ void tq4_prefill_kernel(PrefillArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // The two wavefronts of a SIMD (w and w ^ NW / 2) take the two halves of a step in opposite
+    // orders: one decodes first, the other computes first.  The barrier only separates the two
+    // image buffers, so either order is correct, and the skew lets one wavefront's table decode
+    // and softmax (vector ALU) run under the other's matrix products instead of beside them.
+    const bool late = wave_u >= NW / 2;
     for (int t = 0; t < n_tiles; t += 2) {
-        decode_share(sb, img[1]);
-        valid1 = sb.valid;
-        load_share(sb, min(t + 3, t_last));
+        if (!late) {
+            decode_share(sb, img[1]);
+            valid1 = sb.valid;
+            load_share(sb, min(t + 3, t_last));
+        }
         compute(img[0], t, valid0);
+        if (late) {
+            decode_share(sb, img[1]);
+            valid1 = sb.valid;
+            load_share(sb, min(t + 3, t_last));
+        }
         __syncthreads();
-        decode_share(sa, img[0]);
-        valid0 = sa.valid;
-        load_share(sa, min(t + 4, t_last));
+        if (!late) {
+            decode_share(sa, img[0]);
+            valid0 = sa.valid;
+            load_share(sa, min(t + 4, t_last));
+        }
         compute(img[1], t + 1, valid1 && t + 1 < n_tiles);
+        if (late) {
+            decode_share(sa, img[0]);
+            valid0 = sa.valid;
+            load_share(sa, min(t + 4, t_last));
+        }
         __syncthreads();
     }
 
