@@ -1,7 +1,8 @@
 """Seeded sweep of random shapes through every attention entry point, each checked against the
 oracle (max |err| <= 2e-2, rel-L2 <= 5e-3): page sizes 32..512, groups 1..16, batches 1..5 with
 ragged lengths 1..4,000 (and empty requests), verifier k = 1..8 within the 48-row limit, prefill
-chunks 1..160 over 0..1,500 cached positions, and the INT8 and unfused paths."""
+chunks 1..160 over 0..1,500 cached positions, and the INT8 and unfused paths; the fused appends
+(TQ4 and INT8) equal encode followed by decode bit for bit on the same shapes."""
 import numpy as np
 import pytest
 
@@ -65,6 +66,26 @@ def test_sweep_decode_verify_int8(i):
     torch.cuda.synchronize()
     parity(outv8.cpu(), oracle.int8_attn_verify(pool8, qv64, table, w.seq_lens, synth.SCALE),
            f"int8 verify k={k} " + what)
+    # fused appends (new token at position L - 1 of every non-empty request) against encode followed
+    # by decode, bit for bit, on copies of both pools
+    new = torch.from_numpy(rng.standard_normal((2, w.batch, w.n_kv, 256)).astype(np.float32)).cuda()
+    last = torch.tensor([int(table[b, (L - 1) // w.page_size]) * w.page_size + (L - 1) % w.page_size if L > 0 else -1
+                         for b, L in enumerate(w.seq_lens)], dtype=torch.int32).cuda()
+    fused, ref = to_device(pool), to_device(pool)
+    got = tq4.tq4_attn_decode_append(fused, new[0], new[1], last, q_t.cuda(), tab, seq, max_seq, synth.SCALE)
+    tq4.tq4_encode_pages(ref, new[0], new[1], last)
+    want = tq4.tq4_attn_decode(ref, q_t.cuda(), tab, seq, max_seq, synth.SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want), "append " + what
+    fused8, ref8 = int8_to_device(pool8), int8_to_device(pool8)
+    got8 = tq4.tq4_int8_attn_decode_append(fused8, new[0], new[1], last, q_t.cuda(), tab, seq, max_seq, synth.SCALE)
+    tq4.tq4_int8_encode_pages(ref8, new[0], new[1], last)
+    want8 = tq4.tq4_int8_attn_decode(ref8, q_t.cuda(), tab, seq, max_seq, synth.SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(got8, want8), "int8 append " + what
+    for a, b in ((fused.k_words, ref.k_words), (fused.v_norms, ref.v_norms), (fused8.k_codes, ref8.k_codes),
+                 (fused8.v_scales, ref8.v_scales)):
+        assert torch.equal(a, b), "append records " + what
     # unfused chain against attention over the pages
     kd, vd = tq4.tq4_reconstruct_pages(dpool, tab, seq, max_seq)
     outs = tq4.tq4_sdpa_decode(q_t.cuda(), kd, vd, seq, synth.SCALE)
