@@ -38,7 +38,7 @@ constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kMaxSplits = 256;
 constexpr int kPlanCUs = 256;       // MI355X compute units
 constexpr int kPlanWgsPerCU = 1;    // resident decode workgroups per CU
-constexpr int kMinTilesPerWave = 2;
+constexpr int kMinTilesPerWave = 1;
 constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running maximum is moved
 
 struct DecodeArgs {
