@@ -545,6 +545,35 @@ def cpu_baseline(sample_positions: int):
             "cpu_model": cpu_model, "host_cores_available": len(os.sched_getaffinity(0))}
 
 
+def cpu_encode_baseline(tokens: int = 32768) -> dict:
+    """The oracle's encoder (plain C, fp32 as the encoding rule fixes it) on K and V of `tokens`
+    tokens x 4 KV heads (about 1% of one 212,992-position pool build): once on one core, then with
+    the tokens split over T threads (each its own slots, so the records written are disjoint)."""
+    import numpy as np
+    import oracle
+    import synth
+    from concurrent.futures import ThreadPoolExecutor
+    w0 = synth.WORKLOADS["decode_212k_16l"]
+    w = synth.Workload(w0.wid, "enc_sample", "decode", 1, w0.page_size, w0.pool_pages, seq_lens=(tokens,))
+    slots = synth.used_slots(w, synth.placement(w, 0))
+    k = synth.kv_source(w, 0, tokens, synth.T_K)
+    v = synth.kv_source(w, 0, tokens, synth.T_V)
+    pool = oracle.Pool.empty(w.pool_pages, w.n_kv, w.page_size)
+    t0 = time.perf_counter()
+    oracle.encode_to_pool(pool, k, v, slots)
+    dt1 = time.perf_counter() - t0
+    n_threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    bounds = np.linspace(0, tokens, n_threads + 1).astype(int)
+    parts = [(k[a:b], v[a:b], slots[a:b]) for a, b in zip(bounds[:-1], bounds[1:])]
+    with ThreadPoolExecutor(max_workers=n_threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda kvs: oracle.encode_to_pool(pool, *kvs), parts))
+        dtn = time.perf_counter() - t0
+    vecs = 2 * tokens * w.n_kv
+    return {"vectors_per_s": vecs / dtn, "cores": n_threads, "single_core_vectors_per_s": vecs / dt1,
+            "kind": "oracle", "sample": f"K and V of {tokens} tokens x {w.n_kv} heads (fp32 source)"}
+
+
 def calibration_copy(mib: int, dev) -> None:
     """One device copy of `mib` MiB: the reference dispatch for scaling the PMC byte counters."""
     import torch
@@ -775,6 +804,10 @@ def main() -> int:
         result["cpu_baseline"] = cb = cpu_baseline(args.cpu_sample_positions)
         log(f"cpu baseline: {cb['value']:.0f} positions/s on {cb['cores']} threads "
             f"({cb['single_core_value']:.0f} on one core)")
+        if "encode" in result.get("extra", {}):
+            ce = result["extra"]["encode"]["cpu_oracle"] = cpu_encode_baseline()
+            log(f"cpu oracle encode: {ce['vectors_per_s'] / 1e6:.2f} M vectors/s on {ce['cores']} threads "
+                f"({ce['single_core_vectors_per_s'] / 1e6:.3f} M on one core)")
     print(json.dumps(result), flush=True)
     return 0
 
