@@ -3,9 +3,9 @@
 A step is one decode step of all 16 full-attention layers at 212,992 cached
 positions (196,608 prompt + 16,384 generated; 4 KV heads x 256 dims, 24 bf16
 query heads, 256-token pages shuffled in a 229,376-position pool, one pool per
-layer): per layer, the current token's K and V are encoded into its slot
-(tq4_encode_pages) and the query attends all cached positions
-(tq4_attn_decode).  Inputs are resident in HBM before timing starts.
+layer): per layer, one tq4_attn_decode_append call encodes the current token's
+K and V into its slot and attends all cached positions in the same launch.
+Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """

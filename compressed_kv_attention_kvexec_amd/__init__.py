@@ -78,6 +78,13 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context for allocating a call's missing outputs and workspace on the stream the call runs
+    on: their fills are then ordered before the call's kernels, and the caching allocator reuses
+    the memory only for work ordered after them on that stream."""
+    return torch.cuda.stream(torch.cuda.current_stream() if stream is None else stream)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -131,8 +138,9 @@ def tq4_attn_prefill_workspace_size(prior_len: int, chunk_len: int, n_q_heads: i
 
 
 def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A workspace buffer of at least 256 bytes (the calls do not read its contents on entry)."""
-    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A workspace buffer of at least 256 bytes, allocated on the current stream (the calls do not
+    read its contents on entry, so it is not cleared)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def tq4_attn_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor,
@@ -141,11 +149,12 @@ def tq4_attn_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tenso
                     stream=None) -> torch.Tensor:
     """q [batch][n_q][256] bf16; page_table int32 [batch][stride]; seq_lens int32 [batch]."""
     batch, n_q, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
-                                                                 pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                     pool.page_size), q.device)
     ps = pool.struct()
     check(load_library().tq4_attn_decode(
         ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
@@ -162,11 +171,12 @@ def tq4_attn_decode_append(pool: Tq4LayerPool, k_new, v_new, new_slots: torch.Te
     new_slots[b], the slot of position seq_lens[b] - 1) and attend, in one call."""
     batch, n_q, _ = q.shape
     src = k_new if k_new is not None else v_new
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
-                                                                 pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                     pool.page_size), q.device)
     ps = pool.struct()
     check(load_library().tq4_attn_decode_append(
         ctypes.byref(ps), _ptr(k_new), _ptr(v_new), _dtype_code(src), _ptr(new_slots), _ptr(q), _dtype_code(q),
@@ -181,11 +191,12 @@ def tq4_attn_verify(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tenso
     """q [batch][n_queries][n_q][256] bf16: the last n_queries cached positions of each request
     (seq_lens[b] counts them); query i attends positions 0 .. seq_lens[b] - n_queries + i."""
     batch, n_queries, n_q, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q, pool.n_kv,
-                                                                 pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q, pool.n_kv,
+                                                                     pool.page_size), q.device)
     ps = pool.struct()
     check(load_library().tq4_attn_verify(
         ctypes.byref(ps), _ptr(q), _dtype_code(q), n_queries, _ptr(page_table), int(page_table.shape[1]),
@@ -201,10 +212,11 @@ def tq4_reconstruct_pages(pool: Tq4LayerPool, page_table: torch.Tensor, seq_lens
     batch = int(seq_lens.shape[0])
     shape = (batch, pool.n_kv, int(max_seq_len), HEAD_DIM)
     dev = pool.k_words.device
-    if k_out is None:
-        k_out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
-    if v_out is None:
-        v_out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    with _on(stream):
+        if k_out is None:
+            k_out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+        if v_out is None:
+            v_out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
     ps = pool.struct()
     check(load_library().tq4_reconstruct_pages(
         ctypes.byref(ps), _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), batch, int(max_seq_len),
@@ -222,10 +234,11 @@ def tq4_sdpa_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens:
     """q [batch][n_q][256] bf16 over dense k, v [batch][n_kv][max_seq_len][256] bf16."""
     batch, n_q, _ = q.shape
     n_kv, max_seq = int(k.shape[1]), int(k.shape[2])
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_sdpa_decode_workspace_size(batch, max_seq, n_q, n_kv), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_sdpa_decode_workspace_size(batch, max_seq, n_q, n_kv), q.device)
     check(load_library().tq4_sdpa_decode(
         _ptr(q), _dtype_code(q), _ptr(k), _ptr(v), _dtype_code(k), _ptr(seq_lens), batch, max_seq, n_q, n_kv,
         float(scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -237,11 +250,12 @@ def tq4_attn_prefill_chunk(pool: Tq4LayerPool, q: torch.Tensor, page_table: torc
                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """q [chunk_len][n_q][256] bf16; page_table int32 covering prior_len + chunk_len positions."""
     chunk_len, n_q, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_attn_prefill_workspace_size(prior_len, chunk_len, n_q, pool.n_kv,
-                                                                  pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_attn_prefill_workspace_size(prior_len, chunk_len, n_q, pool.n_kv,
+                                                                      pool.page_size), q.device)
     ps = pool.struct()
     check(load_library().tq4_attn_prefill_chunk(
         ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(prior_len), chunk_len, n_q,
@@ -312,11 +326,12 @@ def tq4_int8_attn_decode(pool: Int8LayerPool, q: torch.Tensor, page_table: torch
                          stream=None) -> torch.Tensor:
     """q [batch][n_q][256] bf16 over INT8 pages; page_table int32 [batch][stride]; seq_lens int32 [batch]."""
     batch, n_q, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_int8_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
-                                                                      pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_int8_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                          pool.page_size), q.device)
     prepare_int8_decode(pool, q, page_table, seq_lens, max_seq_len, scale, out, workspace, stream)()
     return out
 
@@ -328,11 +343,12 @@ def tq4_int8_attn_decode_append(pool: Int8LayerPool, k_new, v_new, new_slots: to
     """INT8 pages: encode each request's new token (k_new / v_new [batch][n_kv][256] fp32 or bf16,
     written at new_slots[b], the slot of position seq_lens[b] - 1) and attend, in one call."""
     batch, n_q, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_int8_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
-                                                                      pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_int8_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                          pool.page_size), q.device)
     prepare_int8_decode_append(pool, k_new, v_new, new_slots, q, page_table, seq_lens, max_seq_len, scale, out,
                                workspace, stream)()
     return out
@@ -349,11 +365,12 @@ def tq4_int8_attn_verify(pool: Int8LayerPool, q: torch.Tensor, page_table: torch
                          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """q [batch][n_queries][n_q][256] bf16: the last n_queries positions of each request, causal."""
     batch, n_queries, n_q, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_int8_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q, pool.n_kv,
-                                                                      pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_int8_attn_verify_workspace_size(batch, max_seq_len, n_queries, n_q, pool.n_kv,
+                                                                          pool.page_size), q.device)
     prepare_int8_verify(pool, q, page_table, seq_lens, max_seq_len, scale, out, workspace, stream)()
     return out
 
@@ -369,11 +386,12 @@ def tq4_int8_attn_prefill_chunk(pool: Int8LayerPool, q: torch.Tensor, page_table
                                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """q [chunk_len][n_q][256] bf16 over INT8 pages; page_table int32 covering prior_len + chunk_len positions."""
     chunk_len, n_q, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = new_workspace(tq4_int8_attn_prefill_workspace_size(prior_len, chunk_len, n_q, pool.n_kv,
-                                                                       pool.page_size), q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_int8_attn_prefill_workspace_size(prior_len, chunk_len, n_q, pool.n_kv,
+                                                                           pool.page_size), q.device)
     prepare_int8_prefill(pool, q, page_table, prior_len, scale, out, workspace, stream)()
     return out
 

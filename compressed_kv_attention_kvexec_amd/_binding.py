@@ -18,7 +18,8 @@ HEADER = os.path.join(ROOT, "include", "tq4.h")
 TQ4_OK = 0
 TQ4_F32, TQ4_BF16, TQ4_F16 = 0, 1, 2
 STATUS_NAMES = {0: "TQ4_OK", 1: "TQ4_ERR_NULL", 2: "TQ4_ERR_SHAPE", 3: "TQ4_ERR_DTYPE",
-                4: "TQ4_ERR_ALIGN", 5: "TQ4_ERR_WORKSPACE", 6: "TQ4_ERR_HIP", 7: "TQ4_ERR_CAPACITY"}
+                4: "TQ4_ERR_ALIGN", 5: "TQ4_ERR_WORKSPACE", 6: "TQ4_ERR_HIP", 7: "TQ4_ERR_CAPACITY",
+                8: "TQ4_ERR_VALUE"}
 TQ4_ERR_CAPACITY = 7
 
 

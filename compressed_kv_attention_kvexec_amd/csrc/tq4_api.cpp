@@ -50,6 +50,11 @@ tq4_status check_heads(int32_t n_q_heads, int32_t n_kv_heads) {
 
 tq4_status from_hip(hipError_t e) { return e == hipSuccess ? TQ4_OK : TQ4_ERR_HIP; }
 
+// The attention kernels take the running maximum of the scaled scores as the maximum of the scores
+// times the scale, and a masked key's score (-inf) times the scale must stay -inf: the scale has
+// to be finite and positive.
+bool scale_ok(float scale) { return scale > 0.0f && scale <= 3.4028234663852886e38f; }
+
 }  // namespace
 
 extern "C" {
@@ -66,6 +71,7 @@ const char *tq4_status_string(tq4_status status) {
         case TQ4_ERR_WORKSPACE: return "workspace missing or too small";
         case TQ4_ERR_HIP: return "HIP runtime error";
         case TQ4_ERR_CAPACITY: return "not enough free pages or memory";
+        case TQ4_ERR_VALUE: return "a scalar argument is out of range (the softmax scale must be finite and > 0)";
     }
     return "unknown status";
 }
@@ -141,6 +147,7 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
     if (q_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
     if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
     if (batch < 1 || batch > 65535 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (!scale_ok(scale)) return TQ4_ERR_VALUE;
     if (pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
     if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
     if (n_queries < 1 || int64_t{n_queries} * (n_q_heads / pool->n_kv_heads) > TQ4_MAX_VERIFY_ROWS)
@@ -264,6 +271,7 @@ tq4_status tq4_sdpa_decode(const void *q, tq4_dtype q_dtype, const void *k, cons
     tq4_status st = check_heads(n_q_heads, n_kv_heads);
     if (st != TQ4_OK) return st;
     if (batch < 1 || batch > 65535 || max_seq_len < 1) return TQ4_ERR_SHAPE;
+    if (!scale_ok(scale)) return TQ4_ERR_VALUE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
         return TQ4_ERR_ALIGN;
     const tq4::DensePlan plan = tq4::plan_dense(batch, max_seq_len, n_q_heads, n_kv_heads);
@@ -308,6 +316,7 @@ tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4
     if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
     if (prior_len < 0 || chunk_len < 1) return TQ4_ERR_SHAPE;
     if (int64_t{prior_len} + chunk_len > (int64_t{1} << 31) - 1) return TQ4_ERR_SHAPE;
+    if (!scale_ok(scale)) return TQ4_ERR_VALUE;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4)) return TQ4_ERR_ALIGN;
     const tq4::PrefillPlan plan = tq4::plan_prefill(prior_len, chunk_len, n_q_heads, pool->n_kv_heads);
     // grid (splits, query blocks, KV heads): 128 query rows per block
@@ -393,6 +402,7 @@ tq4_status int8_common(const tq4_int8_pool *pool, const void *k_new, const void 
     if (q_dtype != TQ4_BF16) return TQ4_ERR_DTYPE;
     if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
     if (batch < 1 || batch > 65535 || max_seq_len < 1 || page_table_stride < 1) return TQ4_ERR_SHAPE;
+    if (!scale_ok(scale)) return TQ4_ERR_VALUE;
     if (pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;
     if (int64_t{max_seq_len} > int64_t{page_table_stride} * pool->page_size) return TQ4_ERR_SHAPE;
     if (n_queries < 1 || int64_t{n_queries} * (n_q_heads / pool->n_kv_heads) > TQ4_MAX_VERIFY_ROWS)
@@ -486,6 +496,7 @@ tq4_status tq4_int8_attn_prefill_chunk(const tq4_int8_pool *pool, const void *q,
     if ((st = check_heads(n_q_heads, pool->n_kv_heads)) != TQ4_OK) return st;
     if (prior_len < 0 || chunk_len < 1) return TQ4_ERR_SHAPE;
     if (int64_t{prior_len} + chunk_len > (int64_t{1} << 31) - 1) return TQ4_ERR_SHAPE;
+    if (!scale_ok(scale)) return TQ4_ERR_VALUE;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4)) return TQ4_ERR_ALIGN;
     const tq4::PrefillPlan plan = tq4::plan_prefill(prior_len, chunk_len, n_q_heads, pool->n_kv_heads);
     if (plan.n_qblocks > 65535 || pool->n_kv_heads > 65535) return TQ4_ERR_SHAPE;

@@ -40,6 +40,21 @@ constexpr int kPlanCUs = 256;       // MI355X compute units
 constexpr int kPlanWgsPerCU = 1;    // resident decode workgroups per CU
 constexpr int kMinTilesPerWave = 1;
 constexpr float kRescaleSlack = 8.0f;  // log2 headroom before the running maximum is moved
+// Value-norm exponent eo of a wavefront (see the P operand below): kNormExpInit while no nonzero
+// norm has been seen (every fp16 norm is >= 2^-24 or 0), at most kNormExpMax (a finite fp16 norm
+// is below 2^16).
+constexpr int kNormExpInit = -40;
+constexpr int kNormExpMax = 9;
+
+// eo for a largest value norm nmx (>= 0): nmx in [2^(eo + 6), 2^(eo + 7)); kNormExpInit for 0,
+// kNormExpMax for +inf or NaN (a norm that overflowed fp16 on encoding, or unwritten bits).
+__device__ __forceinline__ int norm_exponent(float nmx) {
+    if (nmx == 0.f) return kNormExpInit;
+    if (!(nmx <= 65504.f)) return kNormExpMax;
+    int E;
+    frexpf(nmx, &E);  // nmx in [2^(E-1), 2^E)
+    return E - 7;
+}
 
 struct DecodeArgs {
     DecodeParams p;
@@ -263,6 +278,16 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
 #pragma unroll
     for (int t = 0; t < 16; ++t) oacc[t] = float4v{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    // P operand range.  The products O^T += V^T P^T take p_j n_j (softmax weight times value
+    // norm) as fp16.  p_j <= 2^kRescaleSlack, but an fp16 norm reaches 65504 and can be as small
+    // as 2^-24, so the wavefront keeps l_run and oacc relative to 2^eo: its weights are
+    // exp2(s_j - m_run - eo) and P_j = that times n_j.  eo is moved (rarely, in the same branch
+    // that moves the running maximum) so every value norm seen is below 2^(eo + 7): P_j < 2^15
+    // never overflows fp16, and a term whose norm is within 2^-20 of the largest seen is a normal
+    // fp16 number.  The merge below returns l_run and oacc to their true scale (a power of two).
+    int eo = kNormExpInit;
+    // 2^(eo + 7) as fp32 bits: norms are nonnegative, so an unsigned compare of the bits orders them
+    uint32_t n_hi_bits = static_cast<uint32_t>(kNormExpInit + 7 + 127) << 23;
 
     // One tile per step, its register set refilled in place with tile t + NS: the next K is
     // requested as soon as this tile's scores exist, the next V as soon as its P.V products are
@@ -351,13 +376,26 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
         mx = fmaxf(lo, hi);
         lane_pair<32>(mx, lo, hi);
         mx = fmaxf(lo, hi) * fcol;  // fcol > 0
+        // the largest value norm this lane's column sees in the tile
+        const float nmx = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])), fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
+        const bool norm_up = __float_as_uint(nmx) >= n_hi_bits;
         // The reference maximum moves only when a score exceeds it by more than kRescaleSlack (so
-        // exp2(s - m_run) <= 256, well inside fp16): the softmax does not depend on the reference,
-        // and rescaling the 64 accumulators becomes rare.  This lane's accumulators all belong to
-        // column n, so the rescale factor is lane-local.
-        if (__any(mx > m_run + kRescaleSlack)) {
+        // exp2(s - m_run) <= 256): the softmax does not depend on the reference, and rescaling
+        // the 64 accumulators becomes rare.  This lane's accumulators all belong to column n, so
+        // the rescale factor is lane-local.  The same rare branch moves eo.
+        if (__any(mx > m_run + kRescaleSlack || norm_up)) {
+            float f = 1.0f;
+            if (__any(norm_up)) {
+                // a value norm at or above 2^(eo + 7): move eo so the wavefront's largest norm of
+                // the tile is in [2^(eo + 6), 2^(eo + 7)); the sums scale by the power of two
+                const int ne = norm_exponent(__uint_as_float(wave_max_u32(__float_as_uint(nmx), lane)));
+                const int eo_new = __builtin_amdgcn_readfirstlane(min(max(ne, eo + 1), kNormExpMax));
+                f = ldexpf(1.0f, eo - eo_new);
+                eo = eo_new;
+                n_hi_bits = static_cast<uint32_t>(eo + 7 + 127) << 23;
+            }
             const float m_new = fmaxf(m_run, mx);
-            const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+            const float alpha = ((m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f) * f;
             l_run *= alpha;
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt) oacc[tt] *= alpha;
@@ -365,7 +403,7 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
         }
         // m_run is -inf only while every key of the column so far was masked; the floor keeps
         // fcol x - m finite or -inf then, and exp2(-inf) = 0 drops masked keys
-        const float neg_m = -fmaxf(m_run, -FLT_MAX);
+        const float neg_m = -fmaxf(m_run, -FLT_MAX) - static_cast<float>(eo);
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -411,7 +449,7 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
 
     // ---- per-wave softmax totals
     float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-    l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
+    l_tot = ldexpf(l_tot + __shfl_xor(l_tot, 32, kWave), eo);  // true scale: relative to m_run
     __syncthreads();  // table no longer needed
     if (gq == 0) {
         stat_m[wave][n] = m_run;
@@ -420,15 +458,15 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
     __syncthreads();
 
     // ---- merge the waves of each block.  Each lane rescales its accumulators (all of column n)
-    // to the block's maximum over its waves; then a fixed-order tree in LDS adds slots
-    // NS/2 .. NS-1 into 0 .. NS/2-1, and so on down to slot 0.  The LDS image keeps the
+    // to the block's maximum over its waves (and back from 2^eo); then a fixed-order tree in LDS
+    // adds slots NS/2 .. NS-1 into 0 .. NS/2-1, and so on down to slot 0.  The LDS image keeps the
     // accumulator lane layout ([block][slot][register][lane] as 16-byte rows), so every access is
     // conflict-free.  kTreeBlocks blocks fit the table's 64 KiB at once.
     {
         float M = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[blk * NS + j][n]);
-        const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+        const float f = (m_run == -INFINITY) ? 0.f : ldexpf(__builtin_amdgcn_exp2f(m_run - M), eo);
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) oacc[tt] *= f;
     }

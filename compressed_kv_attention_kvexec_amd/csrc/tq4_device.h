@@ -110,4 +110,15 @@ __device__ __forceinline__ void lane_pair(float x, float &lo, float &hi) {
     hi = __builtin_bit_cast(float, r1);
 }
 
+// Maximum of x over the whole wavefront, as a wave-uniform value (lane swaps and DPP, no LDS).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x, int lane) {
+    x = max(x, lane_xor<32>(x, lane));
+    x = max(x, lane_xor<16>(x, lane));
+    x = max(x, lane_xor<8>(x, lane));
+    x = max(x, lane_xor<4>(x, lane));
+    x = max(x, lane_xor<2>(x, lane));
+    x = max(x, lane_xor<1>(x, lane));
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+
 }  // namespace tq4

@@ -41,6 +41,8 @@ constexpr int kPfRowsPerWg = kPfWaves * kPfBlocks * 16;   // 128
 constexpr int kPfTargetWgs = 768;                          // 3 x 256 compute units
 constexpr int kPfAhead = 4;  // operand reads in flight ahead of the MFMAs that use them
 constexpr float kPfRescaleSlack = 8.0f;  // log2 headroom before a running maximum is moved
+constexpr int kPfNormExpMax = 9;  // value-norm exponent for the largest finite fp16 norm (< 2^16)
+constexpr int kPfScanUnroll = 8;  // 4-key groups per lane in flight in the value-norm scan
 
 struct PrefillArgs {
     PrefillParams p;
@@ -119,6 +121,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
     constexpr int E = 16 / NW;  // K operands and V operands each wave decodes per tile
     __shared__ __align__(16) uint32_t lut_mem[kLutWords];
     __shared__ __align__(16) PfTileImage img[2];
+    __shared__ float nmax_sh[NW];
     const PrefillParams &p = a.p;
     const int G = a.group;
     const int s = blockIdx.x, rb = blockIdx.y, g = blockIdx.z;
@@ -225,8 +228,53 @@ void tq4_prefill_kernel(PrefillArgs a) {
             qop[j][ks] = __builtin_bit_cast(half8, v);
         }
     }
+    // ---- P operand range.  The products O^T += V^T P^T take p_j n_j (softmax weight times value
+    // norm) as fp16; p_j <= 2^kPfRescaleSlack, but an fp16 norm reaches 65504 and can be as small
+    // as 2^-24.  The workgroup scans the value norms of its split's keys once (4 per lane and step,
+    // 8-byte loads) and keeps l_run and oacc relative to 2^eo, eo = E - 7 for the largest norm in
+    // [2^(E-1), 2^E): its weights are exp2(s - m_run - eo), so P < 2^15, and a term whose norm is
+    // within 2^-20 of that largest one is a normal fp16 number.  The partials are written back at
+    // their true scale.
+    float nmx = 0.f;
+    {
+        const int n_groups = (key_end - key_begin + 3) >> 2;  // key_begin is a multiple of 32
+        const char *vn = reinterpret_cast<const char *>(p.v_norms);
+        for (int g0 = tid; g0 < n_groups; g0 += kPfScanUnroll * NT) {
+            int pid[kPfScanUnroll];
+#pragma unroll
+            for (int u = 0; u < kPfScanUnroll; ++u) {
+                const int key = key_begin + 4 * min(g0 + u * NT, n_groups - 1);
+                pid[u] = pt[min(key / p.page_size, pt_last)];
+            }
+#pragma unroll
+            for (int u = 0; u < kPfScanUnroll; ++u) {
+                const int grp = g0 + u * NT;
+                const int key = key_begin + 4 * min(grp, n_groups - 1);
+                const bool ok = grp < n_groups && pid[u] >= 0 && pid[u] < p.num_pages;
+                const int64_t rec =
+                    (static_cast<int64_t>(ok ? pid[u] : 0) * p.n_kv + g) * p.page_size + key % p.page_size;
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(vn + rec * 2);
+                const int live = ok ? min(key_end - key, 4) : 0;  // the group's keys inside the split
+                if (live > 0) nmx = fmaxf(nmx, f16lo(w.x));
+                if (live > 1) nmx = fmaxf(nmx, f16hi(w.x));
+                if (live > 2) nmx = fmaxf(nmx, f16lo(w.y));
+                if (live > 3) nmx = fmaxf(nmx, f16hi(w.y));
+            }
+        }
+        // norms are nonnegative: the order of their fp32 bits is their order
+        nmx = __uint_as_float(wave_max_u32(__float_as_uint(nmx), lane));
+        if (lane == 0) nmax_sh[wave_u] = nmx;
+    }
     build_lut<NT>(lut_mem, a.lut_pairs, tid);
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) nmx = fmaxf(nmx, nmax_sh[w]);
+    int eo = 0;  // no nonzero norm: any exponent serves
+    if (nmx > 0.f) {
+        int E;
+        frexpf(nmx, &E);  // nmx in [2^(E-1), 2^E); +inf (a norm that overflowed fp16) takes the cap
+        eo = nmx <= 65504.f ? E - 7 : kPfNormExpMax;
+    }
     const int t_last = max(n_tiles - 1, 0);
     decode_share(sa, img[0]);
     bool valid0 = sa.valid, valid1 = false;  // tiles in img[0] and img[1]
@@ -312,7 +360,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
             lane_pair<32>(mx, lo, hi);
             mx = fmaxf(lo, hi) * fcol[j];  // fcol > 0
             // the reference maximum moves only when a score exceeds it by more than the slack
-            // (exp2(s - m_run) <= 256 stays well inside fp16), so rescaling is rare
+            // (exp2(s - m_run) <= 256), so rescaling is rare
             if (__any(mx > m_run[j] + kPfRescaleSlack)) {
                 const float m_new = fmaxf(m_run[j], mx);
                 const float alpha = (m_new > m_run[j]) ? __builtin_amdgcn_exp2f(m_run[j] - m_new) : 1.0f;
@@ -327,7 +375,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
             }
             // m_run is -inf only while every key of the row so far was masked; the floor keeps
             // fcol x - m finite or -inf then, and exp2(-inf) = 0 drops masked keys
-            const float neg_m = -fmaxf(m_run[j], -FLT_MAX);
+            const float neg_m = -fmaxf(m_run[j], -FLT_MAX) - static_cast<float>(eo);
             float pv[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
@@ -385,13 +433,15 @@ void tq4_prefill_kernel(PrefillArgs a) {
         __syncthreads();
     }
 
-    // ---- partials: lane (gq, n) of block j holds row n, dims 8 (2 (4 gq + r) + c) + i
+    // ---- partials: lane (gq, n) of block j holds row n, dims 8 (2 (4 gq + r) + c) + i; sums and
+    // accumulators go back from 2^eo to their true scale
     float *parts = reinterpret_cast<float *>(ws + a.parts_off);
+    const float escale = ldexpf(1.0f, eo);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int row = row0 + 16 * j + n;
         float l_tot = l_run[j] + __shfl_xor(l_run[j], 16, kWave);
-        l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
+        l_tot = (l_tot + __shfl_xor(l_tot, 32, kWave)) * escale;
         if (row >= a.rows) continue;
         float *dst = parts + ((static_cast<int64_t>(g) * a.rows + row) * a.n_splits + s) * kPfPartial;
 #pragma unroll
@@ -399,7 +449,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) dst[8 * (2 * (4 * gq + r) + c) + i] = oacc[j][8 * c + i][r];
+                for (int i = 0; i < 8; ++i) dst[8 * (2 * (4 * gq + r) + c) + i] = oacc[j][8 * c + i][r] * escale;
         if (gq == 0) {
             dst[kDim] = m_run[j];
             dst[kDim + 1] = l_tot;

@@ -90,7 +90,8 @@ typedef enum tq4_status {
     TQ4_ERR_ALIGN = 4,     /* a pointer is not aligned as documented */
     TQ4_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
     TQ4_ERR_HIP = 6,       /* the HIP runtime reported an error */
-    TQ4_ERR_CAPACITY = 7   /* not enough free pages (or host memory) for the request */
+    TQ4_ERR_CAPACITY = 7,  /* not enough free pages (or host memory) for the request */
+    TQ4_ERR_VALUE = 8      /* a scalar argument is outside its documented range */
 } tq4_status;
 
 typedef enum tq4_dtype {
@@ -165,7 +166,8 @@ size_t tq4_attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_
  *               page_table_stride * page_size; it sets the launch plan.
  *   n_q_heads : a multiple of n_kv_heads with n_q_heads / n_kv_heads <= 16.
  *   batch, n_kv_heads: <= 65535 each (grid dimensions).
- *   scale     : softmax scale applied to q.k (1/16 = 1/sqrt(256) usually).
+ *   scale     : softmax scale applied to q.k (1/16 = 1/sqrt(256) usually);
+ *               finite and > 0, else TQ4_ERR_VALUE.
  *   out       : device [batch][n_q_heads][256] in q_dtype, 16-byte aligned;
  *               out[b][h] = sum_j softmax_j(scale q.k_j) v_j.
  *   workspace : device, >= tq4_attn_decode_workspace_size(...) bytes,
@@ -282,6 +284,7 @@ size_t tq4_sdpa_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_
  *              with 0 positions gets a zero output.
  *   n_q_heads: a multiple of n_kv_heads, n_q_heads / n_kv_heads <= 16;
  *              batch and n_kv_heads <= 65535.
+ *   scale    : finite and > 0, else TQ4_ERR_VALUE.
  *   out      : device bf16 [batch][n_q_heads][256];
  *              out[b][h] = sum_j softmax_j(scale q.k_j) v_j over KV head
  *              h / (n_q_heads / n_kv_heads).
@@ -314,8 +317,12 @@ size_t tq4_attn_prefill_workspace_size(int32_t prior_len, int32_t chunk_len, int
  *   prior_len : >= 0; chunk_len >= 1; chunk_len * (n_q_heads / n_kv_heads) <=
  *               65535 * 128 (query rows, 128 per workgroup row of the grid).
  *   out       : device [chunk_len][n_q_heads][256] in q_dtype.
+ *   scale     : as for tq4_attn_decode (finite and > 0).
  *   workspace : device, >= tq4_attn_prefill_workspace_size(...) bytes,
- *               256-byte aligned, zero-filled before first use (as for decode).
+ *               256-byte aligned.  It holds the rotated queries and per-split
+ *               partial results between the call's kernels; its contents on
+ *               entry do not matter.  Calls sharing a workspace must be
+ *               ordered on one stream.
  */
 tq4_status tq4_attn_prefill_chunk(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
                                   const int32_t *page_table, int32_t prior_len, int32_t chunk_len,

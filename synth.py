@@ -14,7 +14,8 @@ N(0,1) sources and the 1/16 softmax scale are readings stated with each
 workload below.
 
 Seeds: 20260915 + 1000 * workload_id + 10 * layer + tensor, where tensor is
-0 = K source, 1 = V source, 2 = queries, 3 = page placement.
+0 = K source, 1 = V source, 2 = queries, 3 = page placement, 5 / 6 = per-position
+K / V scale factors (mixed-norm pools).
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ import numpy as np
 
 BASE_SEED = 20260915
 T_K, T_V, T_Q, T_PLACE = 0, 1, 2, 3
+T_KSCALE, T_VSCALE = 5, 6
 
 HEAD_DIM = 256
 N_KV = 4
@@ -146,6 +148,13 @@ def kv_source(workload: Workload, layer: int, n_tokens: int, which: int) -> np.n
 def queries_f32(workload: Workload, layer: int, rows: int) -> np.ndarray:
     """N(0,1) fp32 queries [rows][n_q][256]; callers round them to bf16."""
     return normal_f32(seed_of(workload.wid, layer, T_Q), (rows, workload.n_q, HEAD_DIM))
+
+
+def log_uniform_f32(seed: int, n: int, lo: float, hi: float) -> np.ndarray:
+    """n factors drawn log-uniformly from [lo, hi] (numpy PCG64), fp32: per-position scales of the
+    source vectors for pools whose norms span several orders of magnitude."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), n)).astype(np.float32)
 
 
 def bf16_round(x) -> np.ndarray:

@@ -26,7 +26,7 @@ def test_exports_every_declared_function(lib):
     for name in names:
         assert hasattr(lib, name), name
     assert lib.tq4_abi_version() == 1
-    for st in range(8):
+    for st in range(9):
         assert lib.tq4_status_string(st)
 
 
@@ -41,10 +41,36 @@ def test_codebook_matches_oracle_bitwise(lib, oracle_mod):
 
 
 def _decode(lib, pool=None, q=FAKE, q_dtype=B.TQ4_BF16, table=FAKE, stride=64, seq=FAKE, batch=1,
-            max_seq=4000, n_q=24, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+            max_seq=4000, n_q=24, out=FAKE, ws=FAKE, ws_bytes=1 << 30, scale=0.0625):
     pool = _pool() if pool is None else pool
     return lib.tq4_attn_decode(ctypes.byref(pool), q, q_dtype, table, stride, seq, batch, max_seq,
-                               n_q, 0.0625, out, ws, ws_bytes, None)
+                               n_q, scale, out, ws, ws_bytes, None)
+
+
+BAD_SCALES = [0.0, -0.0625, float("nan"), float("inf"), -float("inf")]
+
+
+def test_softmax_scale_must_be_finite_and_positive(lib):
+    """A scale <= 0 or non-finite would turn masked scores (-inf) into NaN or +inf inside the
+    kernels, so every attention entry point rejects it on the host with TQ4_ERR_VALUE."""
+    pool, ipool = _pool(), _i8pool()
+    for sc in BAD_SCALES:
+        assert _decode(lib, scale=sc) == 8, sc
+        assert lib.tq4_attn_verify(ctypes.byref(pool), FAKE, B.TQ4_BF16, 4, FAKE, 64, FAKE, 1, 4000, 24,
+                                   sc, FAKE, FAKE, 1 << 30, None) == 8
+        assert lib.tq4_attn_decode_append(ctypes.byref(pool), FAKE, FAKE, B.TQ4_F32, FAKE, FAKE, B.TQ4_BF16,
+                                          FAKE, 64, FAKE, 1, 4000, 24, sc, FAKE, FAKE, 1 << 30, None) == 8
+        assert lib.tq4_attn_prefill_chunk(ctypes.byref(pool), FAKE, B.TQ4_BF16, FAKE, 100, 28, 24, sc,
+                                          FAKE, FAKE, 1 << 30, None) == 8
+        assert lib.tq4_sdpa_decode(FAKE, B.TQ4_BF16, FAKE, FAKE, B.TQ4_BF16, FAKE, 1, 4000, 24, 4, sc,
+                                   FAKE, FAKE, 1 << 30, None) == 8
+        assert lib.tq4_int8_attn_decode(ctypes.byref(ipool), FAKE, B.TQ4_BF16, FAKE, 64, FAKE, 1, 4000, 24,
+                                        sc, FAKE, FAKE, 1 << 30, None) == 8
+        assert lib.tq4_int8_attn_verify(ctypes.byref(ipool), FAKE, B.TQ4_BF16, 4, FAKE, 64, FAKE, 1, 4000, 24,
+                                        sc, FAKE, FAKE, 1 << 30, None) == 8
+        assert lib.tq4_int8_attn_prefill_chunk(ctypes.byref(ipool), FAKE, B.TQ4_BF16, FAKE, 100, 28, 24, sc,
+                                               FAKE, FAKE, 1 << 30, None) == 8
+    assert "scale" in lib.tq4_status_string(8).decode()
 
 
 def test_decode_validation(lib):

@@ -214,3 +214,36 @@ def test_decode_ignores_garbage_past_the_lengths():
     ref = oracle.attn_decode(pool, q64, table, w.seq_lens, synth.SCALE)
     got = _run(to_device(pool), q_t, table, w.seq_lens, 1000)
     parity(got, ref, "garbage tail")
+
+
+def test_side_stream_without_buffers():
+    """Calls on a side stream with no output or workspace passed allocate them on that stream, so
+    their fills are ordered before the kernels (decode, prefill and reconstruction, whose bf16
+    outputs are zero-filled), while the current stream is kept busy."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    w = synth.Workload(101, "side", "decode", 1, 64, 120, seq_lens=(3000, 700))
+    pool, table = oracle_pool(w)
+    q_t, q64 = bf16_queries(w, 0, w.batch)
+    dpool = to_device(pool)
+    tab = torch.from_numpy(table).cuda()
+    seq = torch.tensor(w.seq_lens, dtype=torch.int32).cuda()
+    side = torch.cuda.Stream()
+    busy = torch.ones(64 << 20, device="cuda")
+    qd = q_t.cuda()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(4):
+        busy.mul_(1.0)  # keeps the current stream occupied while the side stream works
+    out = tq4.tq4_attn_decode(dpool, qd, tab, seq, 3000, synth.SCALE, stream=side)
+    k, v = tq4.tq4_reconstruct_pages(dpool, tab, seq, 3000, stream=side)
+    pq_t, pq64 = bf16_queries(w, 1, 40)
+    pf = tq4.tq4_attn_prefill_chunk(dpool, pq_t.cuda(), tab[0].contiguous(), 2960, synth.SCALE, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    parity(out.cpu(), oracle.attn_decode(pool, q64, table, w.seq_lens, synth.SCALE), "side stream decode")
+    ref_k, _ = oracle.reconstruct(pool, table, w.seq_lens, 3000)
+    got_k = k.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.all(got_k[1, :, 700:] == 0)  # rows past the length keep the zero fill
+    assert (got_k[0] == ref_k[0]).mean() > 0.99
+    ref_pf = oracle.attn_prefill_rows(pool, pq64, np.arange(40), table[0], 2960, synth.SCALE)
+    parity(pf.cpu(), ref_pf, "side stream prefill")

@@ -204,3 +204,41 @@ def test_verify_rows_are_causal(oracle_mod):
             assert np.any(out[b, i] != shorter[0])
     one = oracle_mod.attn_verify(pool, q[:, :1], tables, lens, 1 / 16)
     np.testing.assert_array_equal(one[:, 0], oracle_mod.attn_decode(pool, q[:, 0], tables, lens, 1 / 16))
+
+
+def test_value_scale_equivariance_over_the_fp16_norm_range(oracle_mod):
+    """The record keeps one fp16 norm per vector and attention restores it ("Fitting a 27B-Parameter
+    LLM into 24 GiB of Laptop Memory", section "KVExec: Fused Reconstruction with Layer-Scoped
+    Lifetime"), with no range limit stated.  Scaling every source vector by 2^k leaves the indices
+    unchanged and multiplies each norm by 2^k exactly while it stays a normal fp16 number, so
+    attention with values scaled by 2^k is exactly 2^k times the unscaled result; scaling the keys
+    changes only the scores.  k spans norms from about 2^-13 to 2^15 (the fp16 normal range)."""
+    rng = np.random.default_rng(41)
+    P, n_tok, n_kv = 64, 150, 2
+    k_src = rng.standard_normal((n_tok, n_kv, 256)).astype(np.float32)
+    v_src = rng.standard_normal((n_tok, n_kv, 256)).astype(np.float32)
+    table = rng.permutation(6)[:3].astype(np.int32)
+    slots = (table[np.arange(n_tok) // P] * P + np.arange(n_tok) % P).astype(np.int32)
+    q = _bf16_q(2, 4, 42)
+    base = oracle_mod.Pool.empty(6, n_kv, P)
+    oracle_mod.encode_to_pool(base, k_src, v_src, slots)
+    ref = oracle_mod.attention(base, q, table[None], [0, 0], [n_tok, 77], 1 / 16)
+    n16 = oracle_mod.f16_bits_to_f64(base.v_norms)
+    for k in (-17, -8, 8, 11):
+        pool = oracle_mod.Pool.empty(6, n_kv, P)
+        oracle_mod.encode_to_pool(pool, k_src, np.ldexp(v_src, k).astype(np.float32), slots)
+        np.testing.assert_array_equal(pool.v_words, base.v_words)
+        np.testing.assert_array_equal(pool.k_norms, base.k_norms)
+        np.testing.assert_array_equal(oracle_mod.f16_bits_to_f64(pool.v_norms), np.ldexp(n16, k))
+        out = oracle_mod.attention(pool, q, table[None], [0, 0], [n_tok, 77], 1 / 16)
+        np.testing.assert_array_equal(out, np.ldexp(ref, k))
+    # keys scaled by 2^k: same indices, norms times 2^k, scores times 2^k (a sharper softmax)
+    pool = oracle_mod.Pool.empty(6, n_kv, P)
+    oracle_mod.encode_to_pool(pool, np.ldexp(k_src, 6).astype(np.float32), v_src, slots)
+    np.testing.assert_array_equal(pool.k_words, base.k_words)
+    np.testing.assert_array_equal(oracle_mod.f16_bits_to_f64(pool.k_norms),
+                                  np.ldexp(oracle_mod.f16_bits_to_f64(base.k_norms), 6))
+    sharp = oracle_mod.attention(pool, q[:1], table[None], [0], [n_tok], 1 / 16)
+    q64 = np.asarray(q, np.float64)
+    sharp_by_scale = oracle_mod.attention(base, q64[:1] * 64.0, table[None], [0], [n_tok], 1 / 16)
+    np.testing.assert_allclose(sharp, sharp_by_scale, rtol=1e-12, atol=1e-12)
