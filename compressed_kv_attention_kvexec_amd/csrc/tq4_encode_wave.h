@@ -137,16 +137,13 @@ __device__ __forceinline__ float encode_compute(const float x[4], const float th
     return n32;
 }
 
-// Encodes the vector whose lane values encode_load returned; writes 32 words and the fp16 norm,
-// and returns the fp16 norm's bits (in every lane).
-__device__ __forceinline__ uint32_t encode_values(const float x[4], const float thr[15], uint32_t *words,
-                                                  uint16_t *norm, int lane) {
+// Encodes the vector whose lane values encode_load returned; writes 32 words and the fp16 norm.
+__device__ __forceinline__ void encode_values(const float x[4], const float thr[15], uint32_t *words,
+                                              uint16_t *norm, int lane) {
     uint32_t word;
     const float n32 = encode_compute(x, thr, lane, word);
-    const uint16_t n16 = f32_to_f16_bits(n32);
     if ((lane & 1) == 0) words[lane >> 1] = word;
-    if (lane == 0) *norm = n16;
-    return n16;
+    if (lane == 0) *norm = f32_to_f16_bits(n32);
 }
 
 // src: 256 fp32 (bf16 == false) or bf16 values; writes 32 words and the fp16 norm.

@@ -201,16 +201,6 @@ inline void lut_pairs_from_codebook(uint32_t out[8], const float centroid[16]) {
     }
 }
 
-// fp16 bits of 2^e for a threshold test on fp16 bits of nonnegative values: bits(x) >= the result
-// exactly when x >= 2^e (1 below the subnormal range, so every nonzero value passes; +inf above
-// the largest finite value).
-__host__ __device__ __forceinline__ uint32_t f16_bits_of_pow2(int e) {
-    if (e >= 16) return 0x7c00u;
-    if (e >= -14) return static_cast<uint32_t>(e + 15) << 10;
-    if (e >= -24) return 1u << (e + 24);
-    return 1u;
-}
-
 // Wave-uniform power-of-two scale putting max |y| of a rotated query row in [2^13, 2^14) for
 // the fp16 operand; returns the exponent e (the scale is 2^e).
 __device__ __forceinline__ int q_exponent(float max_abs) {
