@@ -24,7 +24,7 @@ __all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_e
            "tq4_attn_decode_workspace_size", "tq4_attn_decode", "tq4_attn_prefill_workspace_size",
            "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library",
            "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill",
-           "tq4_attn_decode_append", "prepare_decode_append", "tq4_attn_verify_workspace_size",
+           "tq4_attn_decode_append", "prepare_decode_append", "tq4_attn_decode_noalloc", "tq4_attn_verify_workspace_size",
            "tq4_attn_verify", "prepare_verify", "tq4_reconstruct_pages", "tq4_sdpa_decode_workspace_size",
            "tq4_sdpa_decode", "prepare_reconstruct", "prepare_sdpa_decode", "Int8LayerPool",
            "tq4_int8_encode_pages", "tq4_int8_attn_decode_workspace_size", "tq4_int8_attn_decode", "tq4_int8_attn_decode_append", "prepare_int8_decode_append",
@@ -160,6 +160,20 @@ def tq4_attn_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tenso
         ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
         _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tq4_attn_decode_noalloc(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, scale: float,
+                            out: torch.Tensor, stream=None) -> torch.Tensor:
+    """tq4_attn_decode without a workspace (the library's per-device scratch holds the split
+    partials): nothing is allocated, so `out` must be given.  Calls that may overlap on one GPU
+    race on the scratch."""
+    batch, n_q, _ = q.shape
+    ps = pool.struct()
+    check(load_library().tq4_attn_decode_noalloc(
+        ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+        _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale), _ptr(out), _stream(stream)))
     return out
 
 

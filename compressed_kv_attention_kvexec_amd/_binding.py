@@ -69,6 +69,8 @@ def load_library(path: str | None = None):
     lib.tq4_attn_decode_workspace_size.restype = sz
     lib.tq4_attn_decode.argtypes = [pool_p, vp, st, vp, i32, vp, i32, i32, i32, f32, vp, vp, sz, vp]
     lib.tq4_attn_decode.restype = st
+    lib.tq4_attn_decode_noalloc.argtypes = [pool_p, vp, st, vp, i32, vp, i32, i32, i32, f32, vp, vp]
+    lib.tq4_attn_decode_noalloc.restype = st
     lib.tq4_attn_decode_append.argtypes = [pool_p, vp, vp, st, vp, vp, st, vp, i32, vp, i32, i32, i32, f32, vp,
                                            vp, sz, vp]
     lib.tq4_attn_decode_append.restype = st

@@ -135,11 +135,12 @@ size_t tq4_attn_verify_workspace_size(int32_t batch, int32_t max_seq_len, int32_
 
 namespace {
 
+// static_ws: the call brings no workspace and uses the library's device scratch instead.
 tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const void *v_new, tq4_dtype src_dtype,
                          const int32_t *new_slots, bool append, const void *q, tq4_dtype q_dtype,
                          int32_t n_queries, const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
                          int32_t batch, int32_t max_seq_len, int32_t n_q_heads, float scale, void *out,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+                         void *workspace, size_t workspace_bytes, void *stream, bool static_ws = false) {
     tq4_status st = check_pool(pool);
     if (st != TQ4_OK) return st;
     if ((st = check_pool_reads(pool)) != TQ4_OK) return st;
@@ -161,9 +162,18 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
             return TQ4_ERR_ALIGN;
     }
     const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads, n_queries);
-    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
-        return TQ4_ERR_WORKSPACE;
-    if (workspace != nullptr && !aligned(workspace, 256)) return TQ4_ERR_ALIGN;
+    if (static_ws) {
+        if (plan.workspace_bytes > tq4::kStaticScratchBytes) return TQ4_ERR_WORKSPACE;
+        workspace = nullptr;
+        if (plan.workspace_bytes > 0) {
+            const hipError_t e = tq4::static_scratch(&workspace);
+            if (e != hipSuccess) return TQ4_ERR_HIP;
+        }
+    } else {
+        if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+            return TQ4_ERR_WORKSPACE;
+        if (workspace != nullptr && !aligned(workspace, 256)) return TQ4_ERR_ALIGN;
+    }
     tq4::DecodeParams p{};
     p.k_words = pool->k_words;
     p.v_words = pool->v_words;
@@ -201,6 +211,15 @@ tq4_status tq4_attn_decode(const tq4_layer_pool *pool, const void *q, tq4_dtype 
     return decode_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, 1, page_table,
                          page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace,
                          workspace_bytes, stream);
+}
+
+tq4_status tq4_attn_decode_noalloc(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
+                                   const int32_t *page_table, int32_t page_table_stride,
+                                   const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                   int32_t n_q_heads, float scale, void *out, void *stream) {
+    return decode_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, 1, page_table,
+                         page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, nullptr, 0, stream,
+                         true);
 }
 
 tq4_status tq4_attn_verify(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,

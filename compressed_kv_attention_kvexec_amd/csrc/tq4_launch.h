@@ -75,6 +75,12 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStream_t stream);
 
+// Device scratch for decode calls that bring no workspace: 4 MiB, which holds every decode plan
+// with n_q / n_kv <= 6 (at most 3,394,560 bytes, any batch and length).
+constexpr size_t kStaticScratchBytes = size_t{4} << 20;
+// The current device's address of that scratch (looked up once per device).
+hipError_t static_scratch(void **out);
+
 constexpr int kSplitStatPad = 64;  // floats of each statistic row (M, L) in a split partial
 
 // Merge of split-K partials into bf16 rows (shared by the fused decode and the dense path).  The

@@ -183,6 +183,28 @@ tq4_status tq4_attn_decode(const tq4_layer_pool *pool, const void *q, tq4_dtype 
                            size_t workspace_bytes, void *stream);
 
 /*
+ * tq4_attn_decode_noalloc -- tq4_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same arguments without the workspace, the same
+ * kernels and bit-identical results.  The split partials go to a 4 MiB scratch
+ * array inside the library's code object; each GPU the library runs on holds
+ * its own copy until the process ends.  The scratch holds every plan whose
+ * tq4_attn_decode_workspace_size(...) is at most 4 MiB (for example any batch
+ * with n_q_heads / n_kv_heads <= 6); larger plans return TQ4_ERR_WORKSPACE
+ * before anything is enqueued.  The call uses the current device's scratch (the
+ * stream must belong to the current device), calls no allocator, and needs no
+ * clearing (its contents on entry do not matter).  Every call on one GPU shares
+ * that GPU's scratch: calls that may overlap on one GPU (different streams, or
+ * different host threads) race; order them on one stream.
+ * Errors: as tq4_attn_decode, plus TQ4_ERR_HIP if the scratch address cannot be
+ * obtained on first use on a device.
+ */
+tq4_status tq4_attn_decode_noalloc(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
+                                   const int32_t *page_table, int32_t page_table_stride,
+                                   const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                   int32_t n_q_heads, float scale, void *out, void *stream);
+
+/*
  * tq4_attn_decode_append -- the decode step of a model layer in one call: encode
  * each request's new token and attend ([KVX]: the cache is written in TQ4 and
  * read back by the attention that follows).  Results are bit-identical to

@@ -327,3 +327,22 @@ def test_int8_prefill_validation(lib):
     assert call(args(ws_bytes=need - 1)) == 5
     assert call(args(ws=FAKE + 64)) == 4
     assert call(args(q=FAKE + 2)) == 4
+
+
+def test_noalloc_decode_validation(lib):
+    """tq4_attn_decode_noalloc checks its arguments like tq4_attn_decode, and rejects plans larger
+    than its 4 MiB device scratch on the host, before any HIP call."""
+    pool = _pool()
+    call = lambda **kw: lib.tq4_attn_decode_noalloc(
+        ctypes.byref(kw.get("pool", pool)), kw.get("q", FAKE), B.TQ4_BF16, FAKE, kw.get("stride", 64), FAKE,
+        kw.get("batch", 1), kw.get("max_seq", 4000), kw.get("n_q", 24), kw.get("scale", 0.0625), kw.get("out", FAKE),
+        None)
+    assert call(q=None) == 1
+    assert call(out=None) == 1
+    assert call(n_q=22) == 2
+    assert call(scale=0.0) == 8
+    assert call(q=FAKE + 2) == 4
+    # a group of 16 and one long request: the plan needs more than the 4 MiB scratch
+    big = _pool(num_pages=4096, page_size=256, n_kv=4)
+    assert lib.tq4_attn_decode_workspace_size(1, 1_000_000, 64, 4, 256) > 4 << 20
+    assert call(pool=big, stride=4096, max_seq=1_000_000, n_q=64) == 5
