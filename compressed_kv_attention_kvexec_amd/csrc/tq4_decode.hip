@@ -447,109 +447,177 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
     }
     if constexpr (kPaired) __builtin_amdgcn_s_setprio(0);
 
-    // ---- per-wave softmax totals
+    // ---- per-wave softmax totals (the statistics live outside the table, so they are written
+    // before the barrier that retires the table)
     float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
     l_tot = ldexpf(l_tot + __shfl_xor(l_tot, 32, kWave), eo);  // true scale: relative to m_run
-    __syncthreads();  // table no longer needed
     if (gq == 0) {
         stat_m[wave][n] = m_run;
         stat_l[wave][n] = l_tot;
     }
-    __syncthreads();
+    __syncthreads();  // table no longer needed; statistics visible
 
-    // ---- merge the waves of each block.  Each lane rescales its accumulators (all of column n)
-    // to the block's maximum over its waves (and back from 2^eo); then a fixed-order tree in LDS
-    // adds slots NS/2 .. NS-1 into 0 .. NS/2-1, and so on down to slot 0.  The LDS image keeps the
-    // accumulator lane layout ([block][slot][register][lane] as 16-byte rows), so every access is
-    // conflict-free.  kTreeBlocks blocks fit the table's 64 KiB at once.
-    {
-        float M = -INFINITY;
+    // LDS rows of 64 float4 quads of dims, quads swizzled within groups of 8 so that both the
+    // accumulator scatter (lanes (gq, n) -> row n, quad 16 gq + ...) and row reads spread over
+    // the banks
+    auto quad_at = [](int h, int qd) { return h * 64 + (qd ^ ((h + 2 * (qd >> 4)) & 7)); };
+    const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
+    float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
+                 (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
+    float4v *res4;  // single split: the merged rows [ROWS][64 quads] for the inverse rotation
+
+    if constexpr (NB == 1) {
+        // ---- merge the 8 waves in one round.  Every lane takes its column's maximum M and sum
+        // over the waves; each wave writes its rows scaled to M (and back from 2^eo) into its own
+        // LDS slot, and thread (row, quad) adds the 8 slots in a fixed order (the pairing of a
+        // binary tree: slots s and s + 4, then + 2, then + 1), with all 8 reads in flight.
+        // Rows go in passes of kMergeRows (6 x 8 slots x 1 KiB = 48 KiB of the table's space; the
+        // merged rows of a single split take the last 16 KiB).
+        constexpr int kMergeRows = 6;
+        static_assert(NS == 8, "the one-round merge adds 8 slots");
+        float mj[NS], lj[NS];
 #pragma unroll
-        for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[blk * NS + j][n]);
-        const float f = (m_run == -INFINITY) ? 0.f : ldexpf(__builtin_amdgcn_exp2f(m_run - M), eo);
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) oacc[tt] *= f;
-    }
-    if (tid < NCOL) {
-        const int cb = tid >> 4, cn = tid & 15;
-        float M = -INFINITY;
-        for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[cb * NS + j][cn]);
-        float Ls = 0.f;
         for (int j = 0; j < NS; ++j) {
-            const float mj = stat_m[cb * NS + j][cn];
-            Ls += (mj == -INFINITY) ? 0.f : stat_l[cb * NS + j][cn] * __builtin_amdgcn_exp2f(mj - M);
+            mj[j] = stat_m[j][n];
+            lj[j] = stat_l[j][n];
         }
-        resM[tid] = M;
-        resL[tid] = Ls;
-    }
-    float4v *tree = reinterpret_cast<float4v *>(lut_mem);
-    constexpr int kTreeBlocks = (NS >= 2) ? 8 / NS : NB;  // blocks per round: [blocks][NS/2][16][64] rows
+        float M = -INFINITY;
 #pragma unroll
-    for (int b0 = 0; b0 < NB; b0 += kTreeBlocks) {
-        const bool mine = blk >= b0 && blk < b0 + kTreeBlocks;
+        for (int j = 0; j < NS; ++j) M = fmaxf(M, mj[j]);
+        float Ls = 0.f;
 #pragma unroll
-        for (int half = NS / 2; half >= 1; half >>= 1) {
-            // only lanes of query-row columns take part (padding columns are never written out)
-            if (mine && slot >= half && slot < 2 * half && col < ROWS) {
+        for (int j = 0; j < NS; ++j) Ls += (mj[j] == -INFINITY) ? 0.f : lj[j] * __builtin_amdgcn_exp2f(mj[j] - M);
+        if (wave_u == 0 && lane < ROWS) {  // lane < 16: column n = lane
+            resL[lane] = Ls;
+            if (n_active > 1) {
+                dst[lane] = M;
+                dst[kSplitStatPad + lane] = Ls;
+            }
+        }
+        const float f = (m_run == -INFINITY) ? 0.f : ldexpf(__builtin_amdgcn_exp2f(m_run - M), eo);
+        float4v *slots4 = reinterpret_cast<float4v *>(lut_mem);
+        res4 = slots4 + NS * kMergeRows * 64;
+        for (int r0 = 0; r0 < ROWS; r0 += kMergeRows) {
+            const int rp = min(kMergeRows, ROWS - r0);
+            if (col >= r0 && col < r0 + rp) {
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt)
-                    tree[(((blk - b0) * (NS / 2) + slot - half) * 16 + tt) * kWave + lane] = oacc[tt];
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int qd = 16 * gq + 4 * r + 2 * c + hf;
+                            const int t = 8 * c + 4 * hf;
+                            slots4[wave_u * (kMergeRows * 64) + quad_at(col - r0, qd)] =
+                                float4v{oacc[t][r] * f, oacc[t + 1][r] * f, oacc[t + 2][r] * f, oacc[t + 3][r] * f};
+                        }
             }
             __syncthreads();
-            if (mine && slot < half && col < ROWS) {
+            if (tid < rp * 64) {
+                const int rr = tid >> 6, qd = tid & 63;
+                float4v v[NS];
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt)
-                    oacc[tt] += tree[(((blk - b0) * (NS / 2) + slot) * 16 + tt) * kWave + lane];
+                for (int j = 0; j < NS; ++j) v[j] = slots4[j * (kMergeRows * 64) + quad_at(rr, qd)];
+                const float4v sum = ((v[0] + v[4]) + (v[2] + v[6])) + ((v[1] + v[5]) + (v[3] + v[7]));
+                if (n_active > 1)
+                    *reinterpret_cast<float4v *>(dst + 2 * kSplitStatPad + (r0 + rr) * kDim + 4 * qd) = sum;
+                else
+                    res4[quad_at(r0 + rr, qd)] = sum;
             }
             __syncthreads();
         }
-    }
+        if (n_active > 1) return;
+    } else {
+        // ---- merge the waves of each block.  Each lane rescales its accumulators (all of column
+        // n) to the block's maximum over its waves (and back from 2^eo); then a fixed-order tree in
+        // LDS adds slots NS/2 .. NS-1 into 0 .. NS/2-1, and so on down to slot 0.  The LDS image
+        // keeps the accumulator lane layout ([block][slot][register][lane] as 16-byte rows), so
+        // every access is conflict-free.  kTreeBlocks blocks fit the table's 64 KiB at once.
+        {
+            float M = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[blk * NS + j][n]);
+            const float f = (m_run == -INFINITY) ? 0.f : ldexpf(__builtin_amdgcn_exp2f(m_run - M), eo);
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) oacc[tt] *= f;
+        }
+        if (tid < NCOL) {
+            const int cb = tid >> 4, cn = tid & 15;
+            float M = -INFINITY;
+            for (int j = 0; j < NS; ++j) M = fmaxf(M, stat_m[cb * NS + j][cn]);
+            float Ls = 0.f;
+            for (int j = 0; j < NS; ++j) {
+                const float mj = stat_m[cb * NS + j][cn];
+                Ls += (mj == -INFINITY) ? 0.f : stat_l[cb * NS + j][cn] * __builtin_amdgcn_exp2f(mj - M);
+            }
+            resM[tid] = M;
+            resL[tid] = Ls;
+        }
+        float4v *tree = reinterpret_cast<float4v *>(lut_mem);
+        constexpr int kTreeBlocks = (NS >= 2) ? 8 / NS : NB;  // blocks per round: [blocks][NS/2][16][64] rows
+#pragma unroll
+        for (int b0 = 0; b0 < NB; b0 += kTreeBlocks) {
+            const bool mine = blk >= b0 && blk < b0 + kTreeBlocks;
+#pragma unroll
+            for (int half = NS / 2; half >= 1; half >>= 1) {
+                // only lanes of query-row columns take part (padding columns are never written out)
+                if (mine && slot >= half && slot < 2 * half && col < ROWS) {
+#pragma unroll
+                    for (int tt = 0; tt < 16; ++tt)
+                        tree[(((blk - b0) * (NS / 2) + slot - half) * 16 + tt) * kWave + lane] = oacc[tt];
+                }
+                __syncthreads();
+                if (mine && slot < half && col < ROWS) {
+#pragma unroll
+                    for (int tt = 0; tt < 16; ++tt)
+                        oacc[tt] += tree[(((blk - b0) * (NS / 2) + slot) * 16 + tt) * kWave + lane];
+                }
+                __syncthreads();
+            }
+        }
 
-    if (n_active > 1) {
-        // more than one split: the slot-0 wave of each block leaves its rows of
-        // (M[rows], L[rows], O[rows][256]) for the combine kernel; lane (gq, n) holds dims
-        // 8 (2 (4 gq + r) + c) + i of column n in oacc[8 c + i][r]
-        const size_t bg = static_cast<size_t>(b) * p.n_kv + g;
-        float *dst = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + a.parts_off) +
-                     (bg * a.n_splits + s) * static_cast<size_t>(a.partial_floats);
-        if (wave_u == 0 && lane < ROWS) {
-            dst[lane] = resM[lane];
-            dst[kSplitStatPad + lane] = resL[lane];
+        if (n_active > 1) {
+            // more than one split: the slot-0 wave of each block leaves its rows of
+            // (M[rows], L[rows], O[rows][256]) for the combine kernel; lane (gq, n) holds dims
+            // 8 (2 (4 gq + r) + c) + i of column n in oacc[8 c + i][r]
+            if (wave_u == 0 && lane < ROWS) {
+                dst[lane] = resM[lane];
+                dst[kSplitStatPad + lane] = resL[lane];
+            }
+            if (slot == 0 && col < ROWS) {
+                float *row = dst + 2 * kSplitStatPad + col * kDim;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const int d0 = 8 * (2 * (4 * gq + r) + c);
+                        *reinterpret_cast<float4 *>(row + d0) =
+                            make_float4(oacc[8 * c][r], oacc[8 * c + 1][r], oacc[8 * c + 2][r], oacc[8 * c + 3][r]);
+                        *reinterpret_cast<float4 *>(row + d0 + 4) =
+                            make_float4(oacc[8 * c + 4][r], oacc[8 * c + 5][r], oacc[8 * c + 6][r], oacc[8 * c + 7][r]);
+                    }
+            }
+            return;
         }
+
+        // single split: the slot-0 waves write O to LDS as [row][64 quads of dims]
+        res4 = tree;
         if (slot == 0 && col < ROWS) {
-            float *row = dst + 2 * kSplitStatPad + col * kDim;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int d0 = 8 * (2 * (4 * gq + r) + c);
-                    *reinterpret_cast<float4 *>(row + d0) =
-                        make_float4(oacc[8 * c][r], oacc[8 * c + 1][r], oacc[8 * c + 2][r], oacc[8 * c + 3][r]);
-                    *reinterpret_cast<float4 *>(row + d0 + 4) =
-                        make_float4(oacc[8 * c + 4][r], oacc[8 * c + 5][r], oacc[8 * c + 6][r], oacc[8 * c + 7][r]);
-                }
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const int qd = 16 * gq + 4 * r + 2 * c + hf;
+                        res4[quad_at(col, qd)] = float4v{oacc[8 * c + 4 * hf][r], oacc[8 * c + 4 * hf + 1][r],
+                                                         oacc[8 * c + 4 * hf + 2][r], oacc[8 * c + 4 * hf + 3][r]};
+                    }
         }
-        return;
+        __syncthreads();
     }
 
-    // ---- single split: the slot-0 waves write O to LDS as [row][64 quads of dims], quads swizzled
-    // within groups of 8 so both this scatter and the row reads below spread over the banks; then
-    // one wave per row applies the inverse rotation, o = H O / (256 L)
-    auto quad_at = [](int h, int qd) { return h * 64 + (qd ^ ((h + 2 * (qd >> 4)) & 7)); };
-    float4v *res4 = tree;
-    if (slot == 0 && col < ROWS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int qd = 16 * gq + 4 * r + 2 * c + hf;
-                    res4[quad_at(col, qd)] = float4v{oacc[8 * c + 4 * hf][r], oacc[8 * c + 4 * hf + 1][r],
-                                                     oacc[8 * c + 4 * hf + 2][r], oacc[8 * c + 4 * hf + 3][r]};
-                }
-    }
-    __syncthreads();
+    // ---- single split: one wave per row applies the inverse rotation, o = H O / (256 L)
     for (int r = wave_u; r < ROWS; r += NW) {
         const float4v v = res4[quad_at(r, lane)];
         float y[4] = {v[0], v[1], v[2], v[3]};
