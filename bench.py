@@ -498,51 +498,129 @@ def stream_read_probe(device, gib: int = 4, reps: int = 5) -> dict:
     return best
 
 
-def cpu_baseline(sample_positions: int):
-    """The oracle (plain single-threaded C, fp64) on a bounded sample of the same
-    workload: one layer, the first `sample_positions` cached positions, one
-    request, all 24 query heads, timed on one core; then the same call for T
-    layers at once on T threads (T = the cores this process may use, at most
-    16), each layer with its own query over the sample pool (the C call releases
-    the interpreter lock).  `value` is the all-cores rate.  Pool building by the
-    oracle is not timed."""
+def cpu_model_name() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def cpu_threads() -> int:
+    """Threads the CPU oracle runs on: the cores this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_pool_for(w, layer: int = 0):
+    """The oracle's TQ4 pool of a workload's cached positions (seeded synth sources), encoded with
+    the oracle's encoder on all threads (disjoint slots per thread).  Not timed."""
     import numpy as np
     import oracle
     import synth
-    w0 = synth.WORKLOADS["decode_212k_16l"]
-    w = synth.Workload(w0.wid, "sample", "decode", 1, w0.page_size, w0.pool_pages,
-                       seq_lens=(sample_positions,))
-    table = synth.placement(w, 0)
+    from concurrent.futures import ThreadPoolExecutor
+    table = synth.placement(w, layer)
     slots = synth.used_slots(w, table)
     pool = oracle.Pool.empty(w.pool_pages, w.n_kv, w.page_size)
-    oracle.encode_to_pool(pool, synth.kv_source(w, 0, len(slots), synth.T_K),
-                          synth.kv_source(w, 0, len(slots), synth.T_V), slots)
-    q = synth.bf16_round(synth.queries_f32(w, 0, 1)).astype(np.float64)
-    t0 = time.perf_counter()
-    oracle.attn_decode(pool, q, table, [sample_positions], synth.SCALE)
-    dt = time.perf_counter() - t0
-    per_pos_16l = dt / sample_positions * 16  # seconds per cached position over 16 layers
-    # all cores: one layer per thread
+    k = synth.kv_source(w, layer, len(slots), synth.T_K)
+    v = synth.kv_source(w, layer, len(slots), synth.T_V)
+    bounds = np.linspace(0, len(slots), cpu_threads() + 1).astype(int)
+    with ThreadPoolExecutor(max_workers=cpu_threads()) as ex:
+        list(ex.map(lambda ab: oracle.encode_to_pool(pool, k[ab[0]:ab[1]], v[ab[0]:ab[1]], slots[ab[0]:ab[1]]),
+                    zip(bounds[:-1], bounds[1:])))
+    return pool, table
+
+
+def _queries64(w, layer: int, rows: int):
+    import numpy as np
+    import synth
+    return synth.bf16_round(synth.queries_f32(w, layer, rows)).astype(np.float64)
+
+
+def cpu_decode_config(name: str) -> dict:
+    """The oracle (plain C, fp64) on a one-layer decode workload in full: the whole call on one
+    core, then the same call split over KV heads (the oracle's natural unit: one thread per KV head
+    with its query heads) on all threads."""
+    import oracle
+    import synth
     from concurrent.futures import ThreadPoolExecutor
-    n_threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    qs = [synth.bf16_round(synth.queries_f32(w, layer, 1)).astype(np.float64) for layer in range(n_threads)]
-    with ThreadPoolExecutor(max_workers=n_threads) as ex:
+    w = synth.WORKLOADS[name]
+    pool, table = oracle_pool_for(w)
+    q = _queries64(w, 0, w.batch)
+    t0 = time.perf_counter()
+    oracle.attn_decode(pool, q, table, w.seq_lens, synth.SCALE)
+    t1 = time.perf_counter() - t0
+    G = w.n_q // w.n_kv
+    threads = min(cpu_threads(), w.n_kv)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
         t0 = time.perf_counter()
-        list(ex.map(lambda ql: oracle.attn_decode(pool, ql, table, [sample_positions], synth.SCALE), qs))
-        dt_all = time.perf_counter() - t0
-    all_rate = n_threads * sample_positions / 16 / dt_all  # 16-layer positions per second
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": all_rate, "unit": "positions/s", "cores": n_threads, "kind": "oracle",
-            "sample": (f"{n_threads} layers at once, one per thread, each {sample_positions} cached positions x "
-                       f"24 query heads with its own decode query over one sample pool; {dt_all:.2f} s, "
-                       f"scaled to 16 layers"),
-            "seconds": dt_all, "single_core_value": 1.0 / per_pos_16l, "single_core_seconds": dt,
-            "cpu_model": cpu_model, "host_cores_available": len(os.sched_getaffinity(0))}
+        list(ex.map(lambda g: oracle.attn_decode(pool, q, table, w.seq_lens, synth.SCALE, heads=(g * G, (g + 1) * G)),
+                    range(w.n_kv)))
+        tn = time.perf_counter() - t0
+    pos = sum(w.seq_lens)
+    return {"value": pos / tn, "unit": "position-layers/s", "cores": threads, "kind": "oracle",
+            "sample": f"full call ({pos} cached positions x {w.n_q} query heads), one thread per KV head",
+            "seconds": tn, "single_core_value": pos / t1, "single_core_seconds": t1, "cpu_model": cpu_model_name()}
+
+
+def cpu_decode_step(name: str, single_core_layer: bool) -> dict:
+    """The oracle on a 16-layer decode step in full: 16 decode calls (one per layer, each with its
+    own queries over the workload's pool, every cached position of every request), one layer per
+    thread on all threads.  With single_core_layer, one layer's call is also timed on one core and
+    scaled by the layer count (labelled as extrapolated)."""
+    import oracle
+    import synth
+    from concurrent.futures import ThreadPoolExecutor
+    w = synth.WORKLOADS[name]
+    pool, table = oracle_pool_for(w)
+    qs = [_queries64(w, layer, w.batch) for layer in range(w.n_layers)]
+    threads = min(cpu_threads(), w.n_layers)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda ql: oracle.attn_decode(pool, ql, table, w.seq_lens, synth.SCALE), qs))
+        tn = time.perf_counter() - t0
+    pos = sum(w.seq_lens)
+    r = {"value": pos / tn, "unit": "positions/s", "cores": threads, "kind": "oracle",
+         "sample": (f"full step: {w.n_layers} layers x {list(w.seq_lens)} cached positions x {w.n_q} query heads, "
+                    f"one layer per thread over one oracle pool of the workload"),
+         "seconds": tn, "cpu_model": cpu_model_name(), "host_cores_available": len(os.sched_getaffinity(0))}
+    if single_core_layer:
+        t0 = time.perf_counter()
+        oracle.attn_decode(pool, qs[0], table, w.seq_lens, synth.SCALE)
+        t1 = time.perf_counter() - t0
+        r.update({"single_core_value": pos / (t1 * w.n_layers), "single_core_seconds_one_layer": t1,
+                  "single_core_note": f"one layer on one core, scaled by {w.n_layers} layers (extrapolated)"})
+    return r
+
+
+def cpu_prefill_sample(n_rows: int = 32) -> dict:
+    """The oracle on the 2,048-token prefill chunk over 194,560 positions: n_rows sampled query rows
+    (t = 0 and t = 2047 among them) x 24 heads, one thread per (row, KV head); the full chunk's time
+    is extrapolated by attended (query, key) pairs and labelled as such."""
+    import numpy as np
+    import oracle
+    import synth
+    from concurrent.futures import ThreadPoolExecutor
+    w = synth.WORKLOADS["prefill_2k_over_194k"]
+    pool, table = oracle_pool_for(w)
+    rows = np.unique(np.linspace(0, w.chunk_len - 1, n_rows).round().astype(np.int32))
+    q = _queries64(w, 0, w.chunk_len)[rows]
+    G = w.n_q // w.n_kv
+    units = [(i, g) for i in range(len(rows)) for g in range(w.n_kv)]
+    threads = cpu_threads()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda u: oracle.attn_prefill_rows(pool, q[u[0]:u[0] + 1], rows[u[0]:u[0] + 1], table[0],
+                                                       w.prior_len, synth.SCALE, heads=(u[1] * G, (u[1] + 1) * G)),
+                    units))
+        tn = time.perf_counter() - t0
+    pairs_sampled = int(sum(w.prior_len + int(t) + 1 for t in rows))
+    pairs_all = int(sum(w.prior_len + t + 1 for t in range(w.chunk_len)))
+    t_full = tn * pairs_all / pairs_sampled
+    return {"value": w.chunk_len / t_full, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{len(rows)} of {w.chunk_len} query rows (t = 0 .. {w.chunk_len - 1}, evenly spaced) x {w.n_q} "
+                       f"heads, one thread per (row, KV head); the chunk's time extrapolated by attended pairs"),
+            "extrapolated": True, "sample_seconds": tn, "extrapolated_seconds": t_full,
+            "cpu_model": cpu_model_name()}
 
 
 def cpu_encode_baseline(tokens: int = 32768) -> dict:
@@ -585,6 +663,115 @@ def calibration_copy(mib: int, dev) -> None:
     log(f"calibration copy of {mib} MiB done")
 
 
+def run_decode_step(w, dev, steps: int, warmup: int, use_graph: bool = True, calibrate_mib: int = 0,
+                    keep_layers: bool = False):
+    """Time the decode step of a workload: w.n_layers fused calls (encode the new token, attend),
+    one per layer, in order on one stream, as one HIP graph (and eagerly with events around every
+    EVENT_EVERY-th call for the per-call duration).  Returns (result dict, layers or None)."""
+    import torch
+    import compressed_kv_attention_kvexec_amd as tq4
+    import synth
+    build_stats = {}
+    layers = build_layers(w, dev, build_stats)
+    ws_bytes = tq4.tq4_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv, w.page_size)
+    workspace = tq4.new_workspace(ws_bytes, dev)
+    outs = [torch.empty_like(L["q"]) for L in layers]
+    stream = torch.cuda.current_stream()
+    # one fused call per layer: encode the step's new token into the layer's pages, then attend
+    calls = [tq4.prepare_decode_append(L["pool"], L["k_new"], L["v_new"], L["slot_new"], L["q"], L["table"],
+                                       L["seq"], max(w.seq_lens), synth.SCALE, outs[i], workspace, stream)
+             for i, L in enumerate(layers)]
+    timed_layers = list(range(0, w.n_layers, EVENT_EVERY))
+    if calibrate_mib > 0:
+        calibration_copy(calibrate_mib, dev)
+
+    def step(events=None):
+        for i in range(w.n_layers):
+            timed = events is not None and i % EVENT_EVERY == 0
+            if timed:
+                events[i // EVENT_EVERY][0].record(stream)
+            calls[i]()
+            if timed:
+                events[i // EVENT_EVERY][1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"{w.name}: warmup {warmup} steps done")
+
+    # The step as one HIP graph: the same calls captured on a side stream and replayed, which
+    # removes the host launch gaps between them.
+    graph = None
+    if use_graph:
+        gstream = torch.cuda.Stream()
+        gcalls = [tq4.prepare_decode_append(L["pool"], L["k_new"], L["v_new"], L["slot_new"], L["q"], L["table"],
+                                            L["seq"], max(w.seq_lens), synth.SCALE, outs[i], workspace, gstream)
+                  for i, L in enumerate(layers)]
+        try:
+            gstream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(gstream):
+                for c in gcalls:  # one eager pass on the capture stream first
+                    c()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=gstream):
+                for c in gcalls:
+                    c()
+            for _ in range(warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            log(f"{w.name}: captured the step as a HIP graph; {warmup} warmup replays done")
+        except Exception as exc:  # capture unsupported: fall back to the eager step
+            log(f"graph capture failed ({exc}); timing the eager step")
+            graph = None
+
+    def timed_steps(run_step):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            run_step(k)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    elapsed_graph = timed_steps(lambda k: graph.replay()) if graph is not None else None
+    # eager steps with per-call events on every EVENT_EVERY-th layer: the decode call duration
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in timed_layers] for _ in range(steps)]
+    elapsed_eager = timed_steps(lambda k: step(ev[k]))
+    dec_ms = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
+    avg_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
+    elapsed = elapsed_graph if elapsed_graph is not None else elapsed_eager
+    log(f"{w.name}: timed {steps} steps: {elapsed * 1e3 / steps:.3f} ms/step"
+        f"{' (graph)' if elapsed_graph is not None else ''}, eager {elapsed_eager * 1e3 / steps:.3f} ms/step, "
+        f"decode call avg {avg_dec_s * 1e6:.1f} us")
+    for o in outs:  # a cheap guard that the timed work produced results
+        if not torch.isfinite(o.float()).all():
+            raise RuntimeError(f"non-finite decode output ({w.name})")
+    positions = sum(w.seq_lens)  # cached positions per step, each across all layers
+    bytes_launch = decode_algorithmic_bytes(w.seq_lens, w.page_size, w.n_q) + append_bytes(w.batch, w.n_kv)
+    unique = len(synth.used_slots(w, synth.placement(w, 0))) * TQ4_BYTES_PER_POS_LAYER
+    r = {"workload": w.name, "layers": w.n_layers, "batch": w.batch, "cached_positions": list(w.seq_lens),
+         "ms_per_step": elapsed * 1e3 / steps, "positions_per_s": positions / (elapsed / steps),
+         "execution": "hip graph of the step's calls" if elapsed_graph is not None else "eager launches",
+         "eager_ms_per_step": elapsed_eager * 1e3 / steps,
+         "eager_positions_per_s": positions / (elapsed_eager / steps),
+         "avg_launch_us": avg_dec_s * 1e6, "bytes_per_launch": bytes_launch,
+         "achieved_gb_per_s": bytes_launch / avg_dec_s / 1e9,
+         "frac_of_hbm_peak": bytes_launch / avg_dec_s / 1e9 / HBM_PEAK_GBS,
+         "step_gb_per_s": bytes_launch * w.n_layers / (elapsed / steps) / 1e9,
+         "step_frac_of_peak": bytes_launch * w.n_layers / (elapsed / steps) / 1e9 / HBM_PEAK_GBS,
+         "unique_tq4_bytes_per_layer": unique,
+         "decode_calls_timed": len(dec_ms),
+         "timed_calls": f"layers {timed_layers} of every eager timed step (events bracket each)",
+         "encode_build": build_stats}
+    del calls, workspace, graph
+    if not keep_layers:
+        del layers
+        torch.cuda.empty_cache()
+        return r, None
+    return r, layers
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -592,18 +779,20 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_212k_16l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-positions", type=int, default=131072)
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the one-layer cold timings of the other decode workloads")
+                    help="skip the other benchmark workloads (1k and 32k layers, the two-request step)")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip the one-layer cold timings of the packed multi-query verifier")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the reconstruct-then-dense-attention timing")
     ap.add_argument("--no-int8", action="store_true",
                     help="skip the uniform INT8 arm timing")
+    ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth reference points")
     ap.add_argument("--only-config", default="",
                     help="run only the cold one-layer timing of this decode workload (profiler runs)")
+    ap.add_argument("--only-step", default="",
+                    help="run only the timed decode step of this workload, no other leg (profiler runs)")
     ap.add_argument("--int8-only", action="store_true",
                     help="run only the uniform INT8 arm timing (profiler runs)")
     ap.add_argument("--no-graph", action="store_true",
@@ -621,12 +810,9 @@ def main() -> int:
     import compressed_kv_attention_kvexec_amd as tq4
     import synth
 
-    w = synth.WORKLOADS[args.workload]
-    assert w.kind == "decode"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tq4.load_library()
-    log(f"workload {w.name}: {w.n_layers} layers, seq_lens {w.seq_lens}")
     if args.only_config:  # one cold one-layer decode workload alone, for profiler runs
         if args.calibrate_copy_mib > 0:
             calibration_copy(args.calibrate_copy_mib, dev)
@@ -635,137 +821,58 @@ def main() -> int:
     if args.int8_only:  # the INT8 arm alone, for profiler runs
         if args.calibrate_copy_mib > 0:
             calibration_copy(args.calibrate_copy_mib, dev)
-        print(json.dumps({"int8": int8_leg(w.name, dev)}), flush=True)
+        print(json.dumps({"int8": int8_leg(args.workload, dev)}), flush=True)
         return 0
-    build_stats = {}
-    layers = build_layers(w, dev, build_stats)
+    if args.only_step:  # one timed decode step workload alone, for profiler runs
+        r, _ = run_decode_step(synth.WORKLOADS[args.only_step], dev, args.steps, args.warmup, not args.no_graph,
+                               args.calibrate_copy_mib)
+        print(json.dumps({"step": r}), flush=True)
+        return 0
 
-    ws_bytes = tq4.tq4_attn_decode_workspace_size(w.batch, max(w.seq_lens), w.n_q, w.n_kv, w.page_size)
-    workspace = tq4.new_workspace(ws_bytes, dev)
-    outs = [torch.empty_like(L["q"]) for L in layers]
-    stream = torch.cuda.current_stream()
-    # one fused call per layer: encode the step's new token into the layer's pages, then attend
-    calls = [tq4.prepare_decode_append(L["pool"], L["k_new"], L["v_new"], L["slot_new"], L["q"], L["table"],
-                                       L["seq"], max(w.seq_lens), synth.SCALE, outs[i], workspace, stream)
-             for i, L in enumerate(layers)]
-    timed_layers = list(range(0, w.n_layers, EVENT_EVERY))
-
-    if args.calibrate_copy_mib > 0:
-        calibration_copy(args.calibrate_copy_mib, dev)
-
-    def step(events=None):
-        for i in range(w.n_layers):
-            timed = events is not None and i % EVENT_EVERY == 0
-            if timed:
-                events[i // EVENT_EVERY][0].record(stream)
-            calls[i]()
-            if timed:
-                events[i // EVENT_EVERY][1].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done")
-
-    # The step as one HIP graph: the same 16 calls (32 kernels) captured on a side stream and
-    # replayed, which removes the host launch gaps between them.
-    graph = None
-    if not args.no_graph:
-        gstream = torch.cuda.Stream()
-        gcalls = [tq4.prepare_decode_append(L["pool"], L["k_new"], L["v_new"], L["slot_new"], L["q"], L["table"],
-                                            L["seq"], max(w.seq_lens), synth.SCALE, outs[i], workspace, gstream)
-                  for i, L in enumerate(layers)]
-        try:
-            gstream.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(gstream):
-                for c in gcalls:  # one eager pass on the capture stream first
-                    c()
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=gstream):
-                for c in gcalls:
-                    c()
-            for _ in range(args.warmup):
-                graph.replay()
-            torch.cuda.synchronize()
-            log(f"captured the step as a HIP graph; {args.warmup} warmup replays done")
-        except Exception as exc:  # capture unsupported: fall back to the eager step
-            log(f"graph capture failed ({exc}); timing the eager step")
-            graph = None
-
-    def timed_steps(run_step):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(args.steps):
-            run_step(k)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
-    elapsed_graph = timed_steps(lambda k: graph.replay()) if graph is not None else None
-    # eager steps with per-call events on every EVENT_EVERY-th layer: the decode call duration
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in timed_layers] for _ in range(args.steps)]
-    elapsed_eager = timed_steps(lambda k: step(ev[k]))
-    dec_ms = [e0.elapsed_time(e1) for row in ev for (e0, e1) in row]
-    avg_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
-    elapsed = elapsed_graph if elapsed_graph is not None else elapsed_eager
-    log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.3f} ms/step"
-        f"{' (graph)' if elapsed_graph is not None else ''}, eager {elapsed_eager * 1e3 / args.steps:.3f} ms/step, "
-        f"decode call avg {avg_dec_s * 1e6:.1f} us")
-
-    # outputs must be finite (a cheap guard that the timed work produced results)
-    for o in outs:
-        if not torch.isfinite(o.float()).all():
-            raise RuntimeError("non-finite decode output")
-
-    positions = sum(w.seq_lens)  # cached positions per step, each across all layers
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = positions / (elapsed / args.steps)
-    bytes_launch = decode_algorithmic_bytes(w.seq_lens, w.page_size, w.n_q) + append_bytes(w.batch, w.n_kv)
-    achieved = bytes_launch / avg_dec_s / 1e9
-    step_gbs = bytes_launch * w.n_layers / (elapsed / args.steps) / 1e9
-
+    w = synth.WORKLOADS[args.workload]
+    assert w.kind == "decode"
+    log(f"workload {w.name}: {w.n_layers} layers, seq_lens {w.seq_lens}")
+    head, layers = run_decode_step(w, dev, args.steps, args.warmup, not args.no_graph, args.calibrate_copy_mib,
+                                   keep_layers=True)
+    positions = sum(w.seq_lens)
     result = {
-        "metric": METRIC, "value": value, "unit": "positions/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "metric": METRIC, "value": head["positions_per_s"], "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "batch": w.batch,
                    "cached_positions": list(w.seq_lens), "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
                    "head_dim": 256, "page_size": w.page_size, "pool_pages": w.pool_pages,
                    "query_dtype": "bf16"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+        "roofline": {"bound": "hbm", "achieved": head["achieved_gb_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["achieved_gb_per_s"] / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "tq4_attn_decode_append call = tq4_attn_split_kernel<1, 8> + tq4_decode_combine_kernel",
-                     "bytes_per_launch": bytes_launch, "avg_launch_us": avg_dec_s * 1e6},
-        "extra": {"step_hbm_gb_per_s": step_gbs, "step_frac_of_peak": step_gbs / HBM_PEAK_GBS,
-                  "execution": "hip graph of the step's 16 calls" if elapsed_graph is not None else "eager launches",
-                  "eager_ms_per_step": elapsed_eager * 1e3 / args.steps,
-                  "eager_positions_per_s": positions / (elapsed_eager / args.steps),
-                  "decode_calls_timed": len(dec_ms),
-                  "timed_calls": f"layers {timed_layers} of every eager timed step (events bracket each)"},
+                     "bytes_per_launch": head["bytes_per_launch"], "avg_launch_us": head["avg_launch_us"]},
+        "extra": {"step": head, "step_hbm_gb_per_s": head["step_gb_per_s"],
+                  "step_frac_of_peak": head["step_frac_of_peak"]},
     }
     result["extra"]["encode"] = encode_leg(layers[0], w, dev)
     log(f"encode: {result['extra']['encode']['vectors_per_s'] / 1e9:.2f} G vectors/s, "
         f"{result['extra']['encode']['gb_per_s']:.0f} GB/s")
-    del layers, calls, outs, workspace, graph
+    del layers
     torch.cuda.empty_cache()
-    # torch's own reduction over 4 GiB: a reference point for what a library kernel reads, not
-    # the hardware's ceiling (a plain streaming read reaches more)
-    torch_read = torch_sum_read(dev)
-    result["extra"]["torch_sum_read_gb_per_s"] = torch_read
-    log(f"torch.sum over 4 GiB fp32: {torch_read:.0f} GB/s")
-    probe = stream_read_probe(dev)
-    result["extra"]["stream_read_probe"] = probe
-    result["extra"]["decode_frac_of_measured_read"] = result["roofline"]["achieved"] / probe["gb_per_s"]
-    log(f"stream-read probe over 4 GiB: {probe['gb_per_s']:.0f} GB/s ({probe['workgroups']} workgroups); "
-        f"decode call at {100 * result['extra']['decode_frac_of_measured_read']:.1f}% of it")
+    if not args.no_probe:
+        # reference points for plain streaming reads over 4 GiB (not ceilings of this kernel)
+        result["extra"]["torch_sum_read_gb_per_s"] = torch_sum_read(dev)
+        result["extra"]["stream_read_probe"] = stream_read_probe(dev)
+        log(f"torch.sum over 4 GiB fp32: {result['extra']['torch_sum_read_gb_per_s']:.0f} GB/s; stream-read probe "
+            f"{result['extra']['stream_read_probe']['gb_per_s']:.0f} GB/s")
+    configs = result["extra"]["configs"] = {}
     if not args.no_configs:
-        result["extra"]["decode_configs"] = []
-        for name in ("decode_1k_p64", "decode_32k", "decode_2req_shared"):
+        for name in ("decode_1k_p64", "decode_32k"):
             r = decode_config_leg(name, dev)
-            result["extra"]["decode_configs"].append(r)
+            configs[name] = {"gpu": r}
             log(f"{name}: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s (cold)")
+        w3 = synth.WORKLOADS["decode_2req_shared"]
+        r3, _ = run_decode_step(w3, dev, args.steps, args.warmup, not args.no_graph)
+        configs[w3.name] = {"gpu_step": r3, "gpu_one_layer_cold": decode_config_leg(w3.name, dev)}
+        log(f"{w3.name}: {r3['ms_per_step']:.3f} ms/step, {r3['positions_per_s'] / 1e6:.1f} M positions/s, "
+            f"{r3['step_gb_per_s']:.0f} GB/s logical")
     if not args.no_verify:
         result["extra"]["verify"] = []
         for k in (2, 4, 8):
@@ -792,22 +899,35 @@ def main() -> int:
             f"verify k=2/4/8 " + " / ".join(f"{v['us_per_call']:.1f}" for v in r["verify"]) + " us")
     if not args.no_prefill:
         log("prefill leg ...")
-        result["extra"]["prefill"] = prefill_leg(dev)
-        log(f"prefill: {result['extra']['prefill']['ms_per_call']:.3f} ms/call, "
-            f"{result['extra']['prefill']['achieved_tflops']:.1f} TFLOP/s")
+        pf = prefill_leg(dev)
+        result["extra"]["prefill"] = pf
+        configs["prefill_2k_over_194k"] = {"gpu": pf}
+        log(f"prefill: {pf['ms_per_call']:.3f} ms/call, {pf['achieved_tflops']:.1f} TFLOP/s")
         if not args.no_int8:
             r = prefill_leg(dev, int8=True)
             result["extra"]["int8"]["prefill"] = r
             log(f"int8 prefill: {r['ms_per_call']:.3f} ms/call, {r['achieved_tflops']:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_sample_positions} positions ...")
-        result["cpu_baseline"] = cb = cpu_baseline(args.cpu_sample_positions)
-        log(f"cpu baseline: {cb['value']:.0f} positions/s on {cb['cores']} threads "
-            f"({cb['single_core_value']:.0f} on one core)")
+        log("cpu baseline: the oracle on the full 16-layer step ...")
+        result["cpu_baseline"] = cb = cpu_decode_step(w.name, single_core_layer=True)
+        log(f"cpu baseline: {cb['value']:.0f} positions/s on {cb['cores']} threads in {cb['seconds']:.1f} s "
+            f"({cb['single_core_value']:.0f} on one core, extrapolated from one layer)")
         if "encode" in result.get("extra", {}):
             ce = result["extra"]["encode"]["cpu_oracle"] = cpu_encode_baseline()
             log(f"cpu oracle encode: {ce['vectors_per_s'] / 1e6:.2f} M vectors/s on {ce['cores']} threads "
                 f"({ce['single_core_vectors_per_s'] / 1e6:.3f} M on one core)")
+        if not args.no_configs:
+            for name in ("decode_1k_p64", "decode_32k"):
+                configs[name]["cpu_baseline"] = c = cpu_decode_config(name)
+                log(f"cpu baseline {name}: {c['value']:.0f} position-layers/s on {c['cores']} threads "
+                    f"({c['single_core_value']:.0f} on one core)")
+            configs["decode_2req_shared"]["cpu_baseline"] = c = cpu_decode_step("decode_2req_shared", False)
+            log(f"cpu baseline decode_2req_shared: {c['value']:.0f} positions/s on {c['cores']} threads "
+                f"in {c['seconds']:.1f} s")
+        if not args.no_prefill:
+            configs["prefill_2k_over_194k"]["cpu_baseline"] = c = cpu_prefill_sample()
+            log(f"cpu baseline prefill: {c['value']:.2f} query tokens/s (extrapolated from {c['sample_seconds']:.1f} s "
+                f"on {c['cores']} threads)")
     print(json.dumps(result), flush=True)
     return 0
 
