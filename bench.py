@@ -793,6 +793,8 @@ def main() -> int:
                     help="run only the cold one-layer timing of this decode workload (profiler runs)")
     ap.add_argument("--only-step", default="",
                     help="run only the timed decode step of this workload, no other leg (profiler runs)")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the TQ4 chunked-prefill timing (profiler runs)")
     ap.add_argument("--int8-only", action="store_true",
                     help="run only the uniform INT8 arm timing (profiler runs)")
     ap.add_argument("--no-graph", action="store_true",
@@ -822,6 +824,9 @@ def main() -> int:
         if args.calibrate_copy_mib > 0:
             calibration_copy(args.calibrate_copy_mib, dev)
         print(json.dumps({"int8": int8_leg(args.workload, dev)}), flush=True)
+        return 0
+    if args.only_prefill:  # the TQ4 prefill chunk alone, for profiler runs
+        print(json.dumps({"prefill": prefill_leg(dev)}), flush=True)
         return 0
     if args.only_step:  # one timed decode step workload alone, for profiler runs
         r, _ = run_decode_step(synth.WORKLOADS[args.only_step], dev, args.steps, args.warmup, not args.no_graph,
