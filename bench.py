@@ -150,12 +150,13 @@ def encode_leg(layer, w, device, tokens: int = 32768, reps: int = 10):
             "sample": f"{reps} launches of K and V for {tokens} tokens x {w.n_kv} heads (fp32 source)"}
 
 
-def decode_config_leg(name: str, device, reps: int = 20, n_queries: int = 1) -> dict:
+def decode_config_leg(name: str, device, reps: int = 20, n_queries: int = 1, variants=()) -> dict:
     """One layer of a decode workload timed cold: a read of 768 MiB evicts the 256 MB Infinity
     Cache before every call (a read, so no dirty lines are written back during the call).
     Reports the median call time, position-layers/s and GB/s of algorithmic bytes.  With
     n_queries > 1 the call is the packed verifier: the last n_queries positions of each request
-    attend causally in one pass over its pages."""
+    attend causally in one pass over its pages.  variants: decode variants ("valu_rotated",
+    "valu_literal") timed the same way on the same pool, reported under "variants"."""
     import torch
     import compressed_kv_attention_kvexec_amd as tq4
     import synth
@@ -180,25 +181,32 @@ def decode_config_leg(name: str, device, reps: int = 20, n_queries: int = 1) -> 
     if k == 1:
         out = torch.empty_like(q)
         call = tq4.prepare_decode(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, out, ws)
+        vcalls = {v: tq4.prepare_decode_variant(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, v, out, ws)
+                  for v in variants}
     else:
         q = q.reshape(w.batch, k, w.n_q, 256)
         out = torch.empty_like(q)
         call = tq4.prepare_verify(pool, q, tab, seq, max(w.seq_lens), synth.SCALE, out, ws)
     flush = torch.ones(192 << 20, dtype=torch.float32, device=device)
-    for _ in range(3):
-        call()
-    times = []
-    for _ in range(reps):
-        flush.sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / 1e3)
-    if not torch.isfinite(out.float()).all():
-        raise RuntimeError(f"non-finite output ({name}, {k} queries)")
-    t = sorted(times)[reps // 2]
+
+    def cold_median(fn):
+        for _ in range(3):
+            fn()
+        times = []
+        for _ in range(reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+        if not torch.isfinite(out.float()).all():
+            raise RuntimeError(f"non-finite output ({name}, {k} queries)")
+        return sorted(times)[reps // 2]
+
+    vt = {v: cold_median(fn) for v, fn in (vcalls.items() if k == 1 else ())}
+    t = cold_median(call)
     positions = sum(w.seq_lens)
     nbytes = decode_algorithmic_bytes(w.seq_lens, w.page_size, w.n_q) + (k - 1) * w.batch * w.n_q * 256 * 2 * 2
     unique = len(slots) * TQ4_BYTES_PER_POS_LAYER
@@ -212,6 +220,10 @@ def decode_config_leg(name: str, device, reps: int = 20, n_queries: int = 1) -> 
          "timing": f"median of {reps} cold calls (768 MiB read between calls)"}
     if k > 1:
         r.update({"n_queries": k, "query_tokens_per_s": w.batch * k / t, "tflops": flops / t / 1e12})
+    if vt:
+        r["variants"] = {v: {"us_per_call": tv * 1e6, "gb_per_s": nbytes / tv / 1e9,
+                             "frac_of_hbm_peak": nbytes / tv / 1e9 / HBM_PEAK_GBS, "vs_fused": tv / t}
+                         for v, tv in vt.items()}
     return r
 
 
@@ -780,6 +792,10 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_212k_16l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the decode variants without matrix cores (rotated and literal, on the vector ALUs)")
+    ap.add_argument("--variants", default="",
+                    help="with --only-config: also time these decode variants (comma-separated)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other benchmark workloads (1k and 32k layers, the two-request step)")
     ap.add_argument("--no-verify", action="store_true",
@@ -818,7 +834,8 @@ def main() -> int:
     if args.only_config:  # one cold one-layer decode workload alone, for profiler runs
         if args.calibrate_copy_mib > 0:
             calibration_copy(args.calibrate_copy_mib, dev)
-        print(json.dumps({"decode_config": decode_config_leg(args.only_config, dev)}), flush=True)
+        variants = tuple(v for v in args.variants.split(",") if v)
+        print(json.dumps({"decode_config": decode_config_leg(args.only_config, dev, variants=variants)}), flush=True)
         return 0
     if args.int8_only:  # the INT8 arm alone, for profiler runs
         if args.calibrate_copy_mib > 0:
@@ -885,6 +902,11 @@ def main() -> int:
             result["extra"]["verify"].append(r)
             log(f"verify k={k} at {w.seq_lens}: {r['us_per_call']:.1f} us/call, {r['gb_per_s']:.0f} GB/s, "
                 f"{r['tflops']:.1f} TFLOP/s (cold)")
+    if not args.no_ablation:
+        r = decode_config_leg(w.name, dev, variants=("valu_rotated", "valu_literal"))
+        result["extra"]["ablation"] = r
+        log(f"decode ablation at {w.seq_lens}: fused {r['us_per_call']:.1f} us, " + ", ".join(
+            f"{v} {x['us_per_call']:.1f} us ({x['vs_fused']:.2f}x)" for v, x in r["variants"].items()))
     if not args.no_unfused:
         r = unfused_leg(dev)
         r["fused_call_us"] = result["roofline"]["avg_launch_us"]

@@ -20,7 +20,7 @@ import torch
 from ._binding import (TQ4_BF16, TQ4_F16, TQ4_F32, Tq4Error, check, header_functions,
                        load_library, tq4_int8_pool, tq4_layer_pool)
 
-__all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_encode_pages",
+__all__ = ["Tq4LayerPool", "Tq4Error", "tq4_abi_version", "tq4_codebook", "tq4_encode_pages", "tq4_attn_decode_variant", "prepare_decode_variant",
            "tq4_attn_decode_workspace_size", "tq4_attn_decode", "tq4_attn_prefill_workspace_size",
            "tq4_attn_prefill_chunk", "new_workspace", "header_functions", "load_library",
            "PreparedCall", "prepare_encode", "prepare_decode", "prepare_prefill",
@@ -160,6 +160,31 @@ def tq4_attn_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tenso
         ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
         _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+DECODE_VARIANTS = {"fused": 0, "valu_rotated": 1, "valu_literal": 2}
+
+
+def tq4_attn_decode_variant(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, scale: float, variant: str,
+                            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """tq4_attn_decode computed another way: "fused" (the fused kernel), "valu_rotated" (the same
+    rotated-domain arithmetic without matrix cores) or "valu_literal" (per-key fp32 reconstruction
+    and natural-domain attention).  Same workspace as tq4_attn_decode."""
+    batch, n_q, _ = q.shape
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = new_workspace(tq4_attn_decode_workspace_size(batch, max_seq_len, n_q, pool.n_kv,
+                                                                     pool.page_size), q.device)
+    ps = pool.struct()
+    check(load_library().tq4_attn_decode_variant(
+        ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+        _ptr(seq_lens), batch, int(max_seq_len), n_q, float(scale), DECODE_VARIANTS[variant], _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
@@ -443,6 +468,18 @@ def prepare_decode(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor
             _ptr(seq_lens), batch, int(max_seq_len), n_q, ctypes.c_float(scale), _ptr(out),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     return PreparedCall(load_library().tq4_attn_decode, args, (ps, pool, q, page_table, seq_lens, out, workspace))
+
+
+def prepare_decode_variant(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                           max_seq_len: int, scale: float, variant: str, out: torch.Tensor, workspace: torch.Tensor,
+                           stream=None) -> PreparedCall:
+    batch, n_q, _ = q.shape
+    ps = pool.struct()
+    args = (ctypes.byref(ps), _ptr(q), _dtype_code(q), _ptr(page_table), int(page_table.shape[1]),
+            _ptr(seq_lens), batch, int(max_seq_len), n_q, ctypes.c_float(scale), DECODE_VARIANTS[variant],
+            _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    return PreparedCall(load_library().tq4_attn_decode_variant, args,
+                        (ps, pool, q, page_table, seq_lens, out, workspace))
 
 
 def prepare_verify(pool: Tq4LayerPool, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,

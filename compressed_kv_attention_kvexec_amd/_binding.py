@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "TQ4_OK", 1: "TQ4_ERR_NULL", 2: "TQ4_ERR_SHAPE", 3: "TQ4_ERR_
                 4: "TQ4_ERR_ALIGN", 5: "TQ4_ERR_WORKSPACE", 6: "TQ4_ERR_HIP", 7: "TQ4_ERR_CAPACITY",
                 8: "TQ4_ERR_VALUE"}
 TQ4_ERR_CAPACITY = 7
+TQ4_DECODE_FUSED, TQ4_DECODE_VALU_ROTATED, TQ4_DECODE_VALU_LITERAL = 0, 1, 2
 
 
 class Tq4Error(RuntimeError):
@@ -71,6 +72,9 @@ def load_library(path: str | None = None):
     lib.tq4_attn_decode.restype = st
     lib.tq4_attn_decode_noalloc.argtypes = [pool_p, vp, st, vp, i32, vp, i32, i32, i32, f32, vp, vp]
     lib.tq4_attn_decode_noalloc.restype = st
+    lib.tq4_attn_decode_variant.argtypes = [pool_p, vp, st, vp, i32, vp, i32, i32, i32, f32, ctypes.c_int, vp, vp,
+                                            sz, vp]
+    lib.tq4_attn_decode_variant.restype = st
     lib.tq4_attn_decode_append.argtypes = [pool_p, vp, vp, st, vp, vp, st, vp, i32, vp, i32, i32, i32, f32, vp,
                                            vp, sz, vp]
     lib.tq4_attn_decode_append.restype = st

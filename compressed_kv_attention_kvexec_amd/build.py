@@ -20,7 +20,8 @@ ARCH = "gfx950"
 
 PROBE_SOURCES = ["tq4_probe.hip"]
 SOURCES = ["tq4_api.cpp", "tq4_codebook.cpp", "tq4_encode.hip", "tq4_decode.hip", "tq4_prefill.hip",
-           "tq4_dense.hip", "tq4_pages.cpp", "tq4_int8.hip", "tq4_noalloc.hip"]
+           "tq4_dense.hip", "tq4_pages.cpp", "tq4_int8.hip", "tq4_noalloc.hip",
+           "tq4_decode_valu.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-function"]

@@ -140,7 +140,8 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
                          const int32_t *new_slots, bool append, const void *q, tq4_dtype q_dtype,
                          int32_t n_queries, const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
                          int32_t batch, int32_t max_seq_len, int32_t n_q_heads, float scale, void *out,
-                         void *workspace, size_t workspace_bytes, void *stream, bool static_ws = false) {
+                         void *workspace, size_t workspace_bytes, void *stream, bool static_ws = false,
+                         int variant = TQ4_DECODE_FUSED) {
     tq4_status st = check_pool(pool);
     if (st != TQ4_OK) return st;
     if ((st = check_pool_reads(pool)) != TQ4_OK) return st;
@@ -162,6 +163,12 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
             return TQ4_ERR_ALIGN;
     }
     const tq4::DecodePlan plan = tq4::plan_decode(batch, max_seq_len, n_q_heads, pool->n_kv_heads, n_queries);
+    if (variant != TQ4_DECODE_FUSED) {
+        if (variant != TQ4_DECODE_VALU_ROTATED && variant != TQ4_DECODE_VALU_LITERAL) return TQ4_ERR_VALUE;
+        if (append || n_queries != 1) return TQ4_ERR_SHAPE;
+        if (plan.group != 1 && plan.group != 2 && plan.group != 4 && plan.group != 6 && plan.group != 8)
+            return TQ4_ERR_SHAPE;
+    }
     if (static_ws) {
         if (plan.workspace_bytes > tq4::kStaticScratchBytes) return TQ4_ERR_WORKSPACE;
         workspace = nullptr;
@@ -198,6 +205,9 @@ tq4_status decode_common(const tq4_layer_pool *pool, const void *k_new, const vo
         p.new_bf16 = src_dtype == TQ4_BF16;
         p.new_slots = new_slots;
     }
+    if (variant != TQ4_DECODE_FUSED)
+        return from_hip(tq4::launch_decode_valu(p, plan, variant == TQ4_DECODE_VALU_LITERAL,
+                                                static_cast<hipStream_t>(stream)));
     return from_hip(tq4::launch_decode(p, plan, static_cast<hipStream_t>(stream)));
 }
 
@@ -220,6 +230,16 @@ tq4_status tq4_attn_decode_noalloc(const tq4_layer_pool *pool, const void *q, tq
     return decode_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, 1, page_table,
                          page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, nullptr, 0, stream,
                          true);
+}
+
+tq4_status tq4_attn_decode_variant(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
+                                   const int32_t *page_table, int32_t page_table_stride,
+                                   const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                   int32_t n_q_heads, float scale, tq4_decode_variant variant, void *out,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_common(pool, nullptr, nullptr, TQ4_F32, nullptr, false, q, q_dtype, 1, page_table,
+                         page_table_stride, seq_lens, batch, max_seq_len, n_q_heads, scale, out, workspace,
+                         workspace_bytes, stream, false, static_cast<int>(variant));
 }
 
 tq4_status tq4_attn_verify(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype, int32_t n_queries,

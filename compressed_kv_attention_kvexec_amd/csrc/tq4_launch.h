@@ -74,6 +74,10 @@ struct DecodeParams {
 };
 
 hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStream_t stream);
+// Decode on the vector ALUs only (no matrix cores), same plan and partials as launch_decode:
+// rotated-domain scores and values (literal false), or per-key reconstruction in the natural
+// domain (literal true).  Group sizes 1, 2, 4, 6, 8; one query token; no append.
+hipError_t launch_decode_valu(const DecodeParams &p, const DecodePlan &plan, bool literal, hipStream_t stream);
 
 // Device scratch for decode calls that bring no workspace: 4 MiB, which holds every decode plan
 // with n_q / n_kv <= 6 (at most 3,394,560 bytes, any batch and length).

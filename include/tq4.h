@@ -205,6 +205,36 @@ tq4_status tq4_attn_decode_noalloc(const tq4_layer_pool *pool, const void *q, tq
                                    int32_t n_q_heads, float scale, void *out, void *stream);
 
 /*
+ * tq4_attn_decode_variant -- tq4_attn_decode computed another way, to measure
+ * the design choices of the fused kernel.  Same arguments, workspace size and
+ * errors as tq4_attn_decode, plus `variant`:
+ *   TQ4_DECODE_FUSED        the fused kernel itself (tq4_attn_decode).
+ *   TQ4_DECODE_VALU_ROTATED the same rotated-domain arithmetic ([P5]) on the
+ *                           vector ALUs only: fp16 pair dot products with fp32
+ *                           accumulation for the scores, fp32 value sums, one
+ *                           key per half-wavefront, no matrix cores.
+ *   TQ4_DECODE_VALU_LITERAL the reconstruction order of [KVX] taken literally:
+ *                           each key and value vector is rebuilt in fp32
+ *                           (centroid lookup, inverse Hadamard rotation, norm
+ *                           restore) and attention runs in the natural domain.
+ * The two VALU variants take n_q_heads / n_kv_heads in {1, 2, 4, 6, 8}
+ * (TQ4_ERR_SHAPE otherwise); an unknown variant is TQ4_ERR_VALUE.  Results
+ * agree with tq4_attn_decode to the library's attention tolerance, not bit for
+ * bit (the arithmetic differs).
+ */
+typedef enum {
+    TQ4_DECODE_FUSED = 0,
+    TQ4_DECODE_VALU_ROTATED = 1,
+    TQ4_DECODE_VALU_LITERAL = 2
+} tq4_decode_variant;
+
+tq4_status tq4_attn_decode_variant(const tq4_layer_pool *pool, const void *q, tq4_dtype q_dtype,
+                                   const int32_t *page_table, int32_t page_table_stride,
+                                   const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                                   int32_t n_q_heads, float scale, tq4_decode_variant variant, void *out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * tq4_attn_decode_append -- the decode step of a model layer in one call: encode
  * each request's new token and attend ([KVX]: the cache is written in TQ4 and
  * read back by the attention that follows).  Results are bit-identical to

@@ -346,3 +346,21 @@ def test_noalloc_decode_validation(lib):
     big = _pool(num_pages=4096, page_size=256, n_kv=4)
     assert lib.tq4_attn_decode_workspace_size(1, 1_000_000, 64, 4, 256) > 4 << 20
     assert call(pool=big, stride=4096, max_seq=1_000_000, n_q=64) == 5
+
+
+def test_decode_variant_validation(lib):
+    """tq4_attn_decode_variant: the decode checks, then the variant (unknown: TQ4_ERR_VALUE) and
+    the group sizes the vector-ALU kernels are built for (1, 2, 4, 6, 8), all on the host."""
+    pool = _pool()
+    call = lambda **kw: lib.tq4_attn_decode_variant(
+        ctypes.byref(pool), kw.get("q", FAKE), B.TQ4_BF16, FAKE, 64, FAKE, 1, 4000, kw.get("n_q", 24),
+        0.0625, kw.get("variant", B.TQ4_DECODE_VALU_ROTATED), kw.get("out", FAKE), None, 0, None)
+    assert call(q=None) == 1
+    assert call(variant=3) == 8
+    assert call(variant=-1) == 8
+    assert call(n_q=48, variant=B.TQ4_DECODE_VALU_LITERAL) == 2  # group 12
+    assert call(n_q=64, variant=B.TQ4_DECODE_VALU_ROTATED) == 2  # group 16
+    # a valid call would need a workspace for this plan: the workspace check comes last
+    assert lib.tq4_attn_decode_workspace_size(1, 4000, 24, 4, 64) > 0
+    assert call() == 5
+    assert call(variant=B.TQ4_DECODE_FUSED) == 5
