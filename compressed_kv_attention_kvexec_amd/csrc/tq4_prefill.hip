@@ -22,10 +22,14 @@
 //      into fp16 MFMA operands in a double-buffered LDS image, and every
 //      wavefront then feeds its blocks from that image (S^T = K Q^T,
 //      O^T = V^T P^T); online softmax per row with the causal limit; a partial
-//      (O, max, sum) per row and split goes to the workspace;
+//      (O, max, sum) per row and split goes to the workspace.  A wavefront's
+//      decode of the next tile runs inside its work on the current one (table
+//      reads issued during the score products, image writes before the value
+//      products), so the decode's LDS round trip overlaps matrix work;
 //   3. combine: one wavefront per row: merges the splits, inverse rotation,
 //      bf16 output (the same kernel without the rotation serves the INT8 arm).
 #include <cfloat>
+#include <cstddef>
 #include <type_traits>
 
 #include "tq4_device.h"
@@ -53,6 +57,7 @@ struct PrefillArgs {
     uint64_t qrot_off;     // fp16 [chunk_len * n_q][256]
     uint64_t frow_off;     // float [chunk_len * n_q]
     uint64_t parts_off;    // float [n_kv][rows][n_splits][kPfPartial]
+    int32_t page_shift;    // log2(page_size) for a power-of-two page size, else -1
     uint32_t lut_pairs[8];
 };
 
@@ -111,17 +116,58 @@ __global__ __launch_bounds__(256) void tq4_prefill_rotate_kernel(PrefillArgs a) 
 // K-step ks; entry 16 + c * 8 + i the V operand of M-tile (c, i) (lane layouts in tq4_tile.h).
 struct PfTileImage {
     half8 op[32][kWave];
-    float nrm[64];  // K norms of keys 0..31, then V norms
 };
+
+// Rows 2p and 2p + 1 of the 8x8 nibble transpose of tq4_tile.h (in[j] nibble i -> out[i] nibble j),
+// for a row pair p in 0..3 given as two v_perm selectors: half_sel = p >> 1 ? 0x07060302 :
+// 0x05040100 (the high or the low 16 bits of each word), pair_sel = p & 1 ? 0x07030501 :
+// 0x06020400 (which byte of each 16-bit half).  10 instructions where the full transpose takes 38.
+__device__ __forceinline__ void nibble_transpose_pair(const uint32_t in[8], uint32_t half_sel, uint32_t pair_sel,
+                                                      uint32_t &even, uint32_t &odd) {
+    const uint32_t a0 = perm(in[4], in[0], half_sel), a1 = perm(in[5], in[1], half_sel);
+    const uint32_t a2 = perm(in[6], in[2], half_sel), a3 = perm(in[7], in[3], half_sel);
+    const uint32_t b0 = perm(a2, a0, pair_sel), b1 = perm(a3, a1, pair_sel);
+    const uint32_t m = 0x0f0f0f0fu;
+    even = (b0 & m) | ((b1 << 4) & ~m);
+    odd = ((b0 >> 4) & m) | (b1 & ~m);
+}
+
+// The workgroup's LDS in one object: the two operand images (64 KiB), the centroid table at byte
+// 65536, the images' norms (K norms of keys 0..31, then V norms) and the wavefront maxima.  With the
+// table at 2^16, a lane's table address is (index byte) * 256 + 4 * lane + 2^16, which one v_perm
+// builds from the index word and lane_hi = 4 * lane + 2^16 (no base to add).
+template <int NW>
+struct PfShared {
+    PfTileImage img[2];
+    uint32_t lut[kLutWords];
+    float nrm[2][64];
+    float nmax[NW];
+};
+constexpr uint32_t kPfLutOffset = 65536;
+
+// 8 nibbles of one word -> 8 fp16 table values (dim order), the table at kPfLutOffset in lds.
+__device__ __forceinline__ half8 pf_lut_decode(uint32_t w, uint32_t lane_hi, const char *lds) {
+    const uint32_t a0 = perm(w, lane_hi, 0x0c020400u);
+    const uint32_t a1 = perm(w, lane_hi, 0x0c020500u);
+    const uint32_t a2 = perm(w, lane_hi, 0x0c020600u);
+    const uint32_t a3 = perm(w, lane_hi, 0x0c020700u);
+    u32x4 r;
+    r.x = *reinterpret_cast<const uint32_t *>(lds + a0);
+    r.y = *reinterpret_cast<const uint32_t *>(lds + a1);
+    r.z = *reinterpret_cast<const uint32_t *>(lds + a2);
+    r.w = *reinterpret_cast<const uint32_t *>(lds + a3);
+    return __builtin_bit_cast(half8, r);
+}
 
 template <int R, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void tq4_prefill_kernel(PrefillArgs a) {
     constexpr int NT = NW * kWave;
     constexpr int E = 16 / NW;  // K operands and V operands each wave decodes per tile
-    __shared__ __align__(16) uint32_t lut_mem[kLutWords];
-    __shared__ __align__(16) PfTileImage img[2];
-    __shared__ float nmax_sh[NW];
+    __shared__ __align__(16) PfShared<NW> sh;
+    static_assert(offsetof(PfShared<NW>, lut) == kPfLutOffset, "table offset");
+    uint32_t *const lut_mem = sh.lut;
+    float *const nmax_sh = sh.nmax;
     const PrefillParams &p = a.p;
     const int G = a.group;
     const int s = blockIdx.x, rb = blockIdx.y, g = blockIdx.z;
@@ -150,6 +196,11 @@ void tq4_prefill_kernel(PrefillArgs a) {
     const uint32_t k_lane_off = static_cast<uint32_t>(n) * 128u + static_cast<uint32_t>(gq) * 16u +
                                 2048u * mt_w + 64u * h_w + 4u * j_w;
     const uint32_t v_lane_off = static_cast<uint32_t>(gq) * 512u + static_cast<uint32_t>(n) * 8u + 4u * mt_w;
+    // transpose selectors of this wave's row pairs i_w / 2 .. (i_w + E) / 2 - 1 (all in one half)
+    const uint32_t half_sel = (i_w >> 2) ? 0x07060302u : 0x05040100u;
+    uint32_t pair_sel[E / 2];
+#pragma unroll
+    for (int k = 0; k < E / 2; ++k) pair_sel[k] = (((i_w >> 1) + k) & 1) ? 0x07030501u : 0x06020400u;
     const int32_t *pt = p.page_table;
     const int pt_last = (total_keys - 1) / p.page_size;
     using KWords = std::conditional_t<E == 4, u32x4, u32x2>;
@@ -159,10 +210,16 @@ void tq4_prefill_kernel(PrefillArgs a) {
         uint32_t n;
         bool valid;
     };
-    auto load_share = [&](Staging &st, int t) {
+    // page index of a key (wave-uniform; a shift for power-of-two pages)
+    auto page_of = [&](int key) { return a.page_shift >= 0 ? key >> a.page_shift : key / p.page_size; };
+    auto fetch_pid = [&](int t) {  // wave-uniform address: a scalar load
+        return pt[min(page_of(key_begin + t * kTile), pt_last)];
+    };
+    auto load_tile = [&](Staging &st, int t, int pid) {
         const int key0 = key_begin + t * kTile;  // t is clamped by the caller to a tile of this split
-        const int pid = pt[min(key0 / p.page_size, pt_last)];  // wave-uniform address: a scalar load
-        const int64_t rec = tile_rec0(p, g, key0, pid, st.valid);
+        const int off0 = key0 - page_of(key0) * p.page_size;
+        st.valid = pid >= 0 && pid < p.num_pages;  // page IDs outside the pool read page 0, masked
+        const int64_t rec = (static_cast<int64_t>(st.valid ? pid : 0) * p.n_kv + g) * p.page_size + off0;
         const char *kb = reinterpret_cast<const char *>(p.k_words) + rec * (kWords * 4);
         const char *vb = reinterpret_cast<const char *>(p.v_words) + rec * (kWords * 4);
         st.k = *reinterpret_cast<const KWords *>(kb + k_lane_off);
@@ -174,32 +231,38 @@ void tq4_prefill_kernel(PrefillArgs a) {
         const uint16_t *nb = (lane < 32 ? p.k_norms : p.v_norms) + rec + (lane & 31);
         st.n = *nb;
     };
-    const char *lut = reinterpret_cast<const char *>(lut_mem);
-    const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;
-    auto decode_share = [&](const Staging &st, PfTileImage &im) {
-        // all 32 table reads are issued before the first write, so the wave waits for the LDS
-        // round trip once, not once per operand
+    auto load_share = [&](Staging &st, int t) { load_tile(st, t, fetch_pid(t)); };
+    const char *lds = reinterpret_cast<const char *>(&sh);
+    const uint32_t lane_hi = static_cast<uint32_t>(lane) * 4u + kPfLutOffset;
+    // A wave's share of a tile's decode in two parts: the table reads (issued while the matrix
+    // products of the current tile run) and the image writes.
+    struct Decoded {
         half8 d[2 * E];
+        float nrm;
+    };
+    auto decode_issue = [&](const Staging &st, Decoded &dc) {
 #pragma unroll
-        for (int j = 0; j < E; ++j) d[j] = lut_decode(st.k[j], lane4, lut);
-        uint32_t u[8];
-        nibble_transpose8(st.v, u);
-        uint32_t uw[E];  // u[i_w .. i_w + E - 1], picked without indexing by a runtime value
+        for (int j = 0; j < E; ++j) dc.d[j] = pf_lut_decode(st.k[j], lane_hi, lds);
+        uint32_t uw[E];  // rows i_w .. i_w + E - 1 of the transposed words
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            uw[i] = u[i];
+        for (int i = 0; i < E; i += 2) nibble_transpose_pair(st.v, half_sel, pair_sel[i / 2], uw[i], uw[i + 1]);
 #pragma unroll
-            for (int c = 1; c < 8 / E; ++c) uw[i] = (i_w == c * E) ? u[c * E + i] : uw[i];
-        }
+        for (int i = 0; i < E; ++i) dc.d[E + i] = pf_lut_decode(uw[i], lane_hi, lds);
+        dc.nrm = f16_bits_to_f32(static_cast<uint16_t>(st.n));
+    };
+    auto decode_write = [&](const Decoded &dc, int b) {
+        PfTileImage &im = sh.img[b];
 #pragma unroll
-        for (int i = 0; i < E; ++i) d[E + i] = lut_decode(uw[i], lane4, lut);
-        const float nrm = f16_bits_to_f32(static_cast<uint16_t>(st.n));
+        for (int j = 0; j < E; ++j) im.op[e0 + j][lane] = dc.d[j];
+#pragma unroll
+        for (int i = 0; i < E; ++i) im.op[16 + e0 + i][lane] = dc.d[E + i];
+        sh.nrm[b][lane] = dc.nrm;  // every wave writes the same values
+    };
+    auto decode_share = [&](const Staging &st, int b) {
+        Decoded dc;
+        decode_issue(st, dc);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < E; ++j) im.op[e0 + j][lane] = d[j];
-#pragma unroll
-        for (int i = 0; i < E; ++i) im.op[16 + e0 + i][lane] = d[E + i];
-        im.nrm[lane] = nrm;  // every wave writes the same values
+        decode_write(dc, b);
     };
 
     // two staging sets, each refilled in place two tiles ahead of its decode
@@ -244,7 +307,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int u = 0; u < kPfScanUnroll; ++u) {
                 const int key = key_begin + 4 * min(g0 + u * NT, n_groups - 1);
-                pid[u] = pt[min(key / p.page_size, pt_last)];
+                pid[u] = pt[min(page_of(key), pt_last)];
             }
 #pragma unroll
             for (int u = 0; u < kPfScanUnroll; ++u) {
@@ -252,7 +315,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
                 const int key = key_begin + 4 * min(grp, n_groups - 1);
                 const bool ok = grp < n_groups && pid[u] >= 0 && pid[u] < p.num_pages;
                 const int64_t rec =
-                    (static_cast<int64_t>(ok ? pid[u] : 0) * p.n_kv + g) * p.page_size + key % p.page_size;
+                    (static_cast<int64_t>(ok ? pid[u] : 0) * p.n_kv + g) * p.page_size + key - page_of(key) * p.page_size;
                 const u32x2 w = *reinterpret_cast<const u32x2 *>(vn + rec * 2);
                 const int live = ok ? min(key_end - key, 4) : 0;  // the group's keys inside the split
                 if (live > 0) nmx = fmaxf(nmx, f16lo(w.x));
@@ -276,7 +339,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
         eo = nmx <= 65504.f ? E - 7 : kPfNormExpMax;
     }
     const int t_last = max(n_tiles - 1, 0);
-    decode_share(sa, img[0]);
+    decode_share(sa, 0);
     bool valid0 = sa.valid, valid1 = false;  // tiles in img[0] and img[1]
     load_share(sb, min(1, t_last));
     load_share(sa, min(2, t_last));
@@ -292,12 +355,11 @@ void tq4_prefill_kernel(PrefillArgs a) {
         l_run[j] = 0.f;
     }
 
-    // Tiles in pairs: decode this wave's share of tile t + 1 into the other buffer, request its share
-    // of tile t + 3 into the staging set just consumed, then run all R blocks on tile t from the
-    // shared image; one barrier per tile.  A pair's second tile past the end is computed fully
-    // masked (its image holds a clamped, valid tile), which keeps every wave's loads and barriers
-    // the same.
-    auto compute = [&](const PfTileImage &im, int t, bool valid) {
+    // Tile t for all R blocks from image b: scores, online softmax, value products.  mid_qk runs once
+    // every score operand is requested, before_pv between the softmax and the value products.
+    auto compute = [&](int b, int t, bool valid, auto &&mid_qk, auto &&before_pv) {
+        const PfTileImage &im = sh.img[b];
+        const float *nrm = sh.nrm[b];
         const int key0 = key_begin + t * kTile;
         // ---- scores for all R blocks.  Operands are read kPfAhead entries ahead of their MFMAs
         // and the order is pinned, so only a few operands are live at once (the compiler would
@@ -316,15 +378,19 @@ void tq4_prefill_kernel(PrefillArgs a) {
                 sacc[j][e >> 3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(opb[e % (kPfAhead + 1)], qop[j][e & 7],
                                                                          sacc[j][e >> 3], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+            if (e == 15 - kPfAhead) {  // every score operand is requested: start the next tile's decode
+                mid_qk();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // the first V operands are requested before the softmax
 #pragma unroll
         for (int e = 0; e < kPfAhead; ++e) opb[e] = im.op[16 + e][lane];
         // lane holds keys sigma(j): j < 4 -> 4 gq + j, else 16 + 4 gq + j - 4
-        const float4 kn0 = *reinterpret_cast<const float4 *>(&im.nrm[4 * gq]);
-        const float4 kn1 = *reinterpret_cast<const float4 *>(&im.nrm[16 + 4 * gq]);
-        const float4 nv0 = *reinterpret_cast<const float4 *>(&im.nrm[32 + 4 * gq]);
-        const float4 nv1 = *reinterpret_cast<const float4 *>(&im.nrm[48 + 4 * gq]);
+        const float4 kn0 = *reinterpret_cast<const float4 *>(&nrm[4 * gq]);
+        const float4 kn1 = *reinterpret_cast<const float4 *>(&nrm[16 + 4 * gq]);
+        const float4 nv0 = *reinterpret_cast<const float4 *>(&nrm[32 + 4 * gq]);
+        const float4 nv1 = *reinterpret_cast<const float4 *>(&nrm[48 + 4 * gq]);
         const float kn[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
         const float nv[8] = {nv0.x, nv0.y, nv0.z, nv0.w, nv1.x, nv1.y, nv1.z, nv1.w};
         // ---- online softmax per block, probabilities as the P^T operand
@@ -390,6 +456,8 @@ void tq4_prefill_kernel(PrefillArgs a) {
             pr.w = pack_f16x2(pv[6], pv[7]);
             pop[j] = __builtin_bit_cast(half8, pr);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        before_pv();
         // ---- O^T += V^T P^T for all R blocks, operands pipelined as for the scores
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -401,36 +469,29 @@ void tq4_prefill_kernel(PrefillArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // The two wavefronts of a SIMD (w and w ^ NW / 2) take the two halves of a step in opposite
-    // orders: one decodes first, the other computes first.  The barrier only separates the two
-    // image buffers, so either order is correct, and the skew lets one wavefront's table decode
-    // and softmax (vector ALU) run under the other's matrix products instead of beside them.
-    const bool late = wave_u >= NW / 2;
+    // Each step computes tile t from one image while this wave's share of tile t + 1 is decoded into
+    // the other: the table reads are issued once the score operands are requested, and the image
+    // writes go out before the value products, so the decode's LDS round trip overlaps the matrix
+    // work instead of preceding it.  The staging set just decoded is refilled with tile t + 3 (its
+    // page ID requested at the start of the step).  One barrier per tile; tiles go in pairs, and a
+    // pair's second tile past the end is computed fully masked (its image holds a clamped, valid
+    // tile), which keeps every wave's loads and barriers the same.
+    auto step = [&](Staging &st, int t_next, int b_dec, int b_cmp, int t) {
+        Decoded dc;
+        bool &vdec = b_dec ? valid1 : valid0;
+        const bool vcmp = (b_cmp ? valid1 : valid0) && t < n_tiles;
+        const int tn = min(t_next, t_last);
+        const int pid_next = fetch_pid(tn);  // requested now, used after the softmax
+        compute(b_cmp, t, vcmp, [&] { decode_issue(st, dc); }, [&] {
+            decode_write(dc, b_dec);
+            vdec = st.valid;
+            load_tile(st, tn, pid_next);  // the staging set is free again: refill it before the value products
+        });
+        __syncthreads();
+    };
     for (int t = 0; t < n_tiles; t += 2) {
-        if (!late) {
-            decode_share(sb, img[1]);
-            valid1 = sb.valid;
-            load_share(sb, min(t + 3, t_last));
-        }
-        compute(img[0], t, valid0);
-        if (late) {
-            decode_share(sb, img[1]);
-            valid1 = sb.valid;
-            load_share(sb, min(t + 3, t_last));
-        }
-        __syncthreads();
-        if (!late) {
-            decode_share(sa, img[0]);
-            valid0 = sa.valid;
-            load_share(sa, min(t + 4, t_last));
-        }
-        compute(img[1], t + 1, valid1 && t + 1 < n_tiles);
-        if (late) {
-            decode_share(sa, img[0]);
-            valid0 = sa.valid;
-            load_share(sa, min(t + 4, t_last));
-        }
-        __syncthreads();
+        step(sb, t + 3, 1, 0, t);
+        step(sa, t + 4, 0, 1, t + 1);
     }
 
     // ---- partials: lane (gq, n) of block j holds row n, dims 8 (2 (4 gq + r) + c) + i; sums and
@@ -516,6 +577,7 @@ hipError_t launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipSt
     a.qrot_off = 0;
     a.frow_off = ((qrows * kDim * 2 + 255) / 256) * 256;
     a.parts_off = plan.counters_bytes;
+    a.page_shift = (p.page_size & (p.page_size - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(p.page_size)) : -1;
     lut_pairs_from_codebook(a.lut_pairs, codebook().centroid);
     const int64_t rot_blocks = (static_cast<int64_t>(qrows) + 3) / 4;
     const int64_t comb_blocks = (static_cast<int64_t>(p.n_kv) * a.rows + 3) / 4;
