@@ -59,20 +59,43 @@ __device__ __forceinline__ void load16(const char *vec, int g, float x[16]) {
     }
 }
 
+// The value of lane (lane ^ M) for M in {1, 2, 4, 8} inside a 16-lane row, as DPP moves whose
+// source lane always exists (so no old value has to be kept in the destination).  For M = 4: the
+// half-row mirror (lane i of each 8 reads lane 7 - i) and then the quad reversal (lane j of each 4
+// reads lane 3 - j).
+template <int M>
+__device__ __forceinline__ float row_xor(float x, int) {
+    const int v = __builtin_bit_cast(int, x);
+    int r;
+    if constexpr (M == 1) {
+        r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm 1,0,3,2
+    } else if constexpr (M == 2) {
+        r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm 2,3,0,1
+    } else if constexpr (M == 4) {
+        r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true), 0x1B, 0xF, 0xF, true);
+    } else {
+        static_assert(M == 8, "row_xor: M is 1, 2, 4 or 8");
+        r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);  // row_ror:8
+    }
+    return __builtin_bit_cast(float, r);
+}
+
 // Tree stride 16 M: element e of lane g and of lane g ^ M (commutative, so both lanes of the pair
 // get s[i] + s[i + stride]).
 template <int M>
 __device__ __forceinline__ void norm_cross16(float s[16], int lane) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = s[e] + lane_xor<M>(s[e], lane);
+    for (int e = 0; e < 16; ++e) s[e] = s[e] + row_xor<M>(s[e], lane);
 }
 
-// Hadamard stage 16 M: lower lane of the pair lo + hi, upper lane lo - hi = lo + (-hi).
+// Hadamard stage 16 M: lower lane of the pair lo + hi, upper lane lo - hi = lo + (-hi).  Both are
+// one fused multiply-add, own * (+1 or -1) + partner: the product is exact, so the result is the
+// rounded sum of the same two values.
 template <int M>
 __device__ __forceinline__ void hadamard_cross16(float y[16], int lane) {
-    const bool upper = (lane & M) != 0;
+    const float sgn = (lane & M) != 0 ? -1.0f : 1.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) y[e] = lane_xor<M>(y[e], lane) + flip_if(y[e], upper);
+    for (int e = 0; e < 16; ++e) y[e] = __builtin_fmaf(y[e], sgn, row_xor<M>(y[e], lane));
 }
 
 // Encodes the vector whose 16-lane group holds x (lane g: dims 16 g ..); returns the fp32 norm and
