@@ -454,7 +454,7 @@ def prefill_leg(device, reps: int = 3, int8: bool = False):
 
 def torch_sum_read(device, gib: int = 4, reps: int = 5) -> float:
     """Read rate of torch's fp32 sum over `gib` GiB (far beyond the 256 MB Infinity Cache), GB/s,
-    best of `reps`: what a library reduction kernel reads, below the hardware's streaming ceiling."""
+    best of `reps`: what a library reduction kernel reads (a reference point)."""
     import torch
     x = torch.ones(gib * (1 << 30) // 4, dtype=torch.float32, device=device)
     x.sum()
@@ -473,9 +473,10 @@ def torch_sum_read(device, gib: int = 4, reps: int = 5) -> float:
 
 
 def stream_read_probe(device, gib: int = 4, reps: int = 5) -> dict:
-    """Read rate of the streaming-read probe (libtq4probe.so, include/tq4_probe.h) over `gib` GiB,
-    best over grid sizes and `reps` repetitions: the read bandwidth this device reaches in
-    practice, the measured ceiling for memory-bound kernels."""
+    """Read rate of the streaming-read probe (libtq4probe.so, compressed_kv_attention_kvexec_amd/csrc/tq4_probe.h)
+    over `gib` GiB, best over grid sizes and `reps` repetitions: what a plain grid-stride read
+    kernel reaches on this device.  A reference point, not a ceiling (the decode loop streams
+    faster), so no figure is reported as a fraction of it."""
     import ctypes
     import torch
     from compressed_kv_attention_kvexec_amd import build as hipbuild

@@ -3,9 +3,10 @@
  * (gfx950), built as its own library (libtq4probe.so) beside libtq4.so.
  *
  * It is measurement support, not part of the attention path: a benchmark
- * times it to state the read rate this device actually reaches, next to the
- * vendor's 8 TB/s figure, when it reports how close a memory-bound kernel
- * comes to its roofline.
+ * times it to report the read rate a plain grid-stride read kernel reaches on
+ * this device, beside the vendor's 8 TB/s figure.  It is a reference point,
+ * not a ceiling: a kernel with more loads in flight per wavefront (the decode
+ * loop) streams faster.
  */
 #ifndef TQ4_PROBE_H
 #define TQ4_PROBE_H

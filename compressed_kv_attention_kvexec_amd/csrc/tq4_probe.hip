@@ -1,4 +1,4 @@
-// tq4_probe.hip -- streaming-read bandwidth probe (include/tq4_probe.h): a plain grid-stride read
+// tq4_probe.hip -- streaming-read bandwidth probe (tq4_probe.h): a plain grid-stride read
 // with four 16-byte loads in flight per thread, 256 threads per workgroup.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
