@@ -80,14 +80,6 @@ __device__ __forceinline__ float row_xor(float x, int) {
     return __builtin_bit_cast(float, r);
 }
 
-// Tree stride 16 M: element e of lane g and of lane g ^ M (commutative, so both lanes of the pair
-// get s[i] + s[i + stride]).
-template <int M>
-__device__ __forceinline__ void norm_cross16(float s[16], int lane) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = s[e] + row_xor<M>(s[e], lane);
-}
-
 // Hadamard stage 16 M: lower lane of the pair lo + hi, upper lane lo - hi = lo + (-hi).  Both are
 // one fused multiply-add, own * (+1 or -1) + partner: the product is exact, so the result is the
 // rounded sum of the same two values.
@@ -98,26 +90,42 @@ __device__ __forceinline__ void hadamard_cross16(float y[16], int lane) {
     for (int e = 0; e < 16; ++e) y[e] = __builtin_fmaf(y[e], sgn, row_xor<M>(y[e], lane));
 }
 
+// Row stride (floats) of the squares' transpose area: 17, so the 16 lanes of a row and the four
+// vectors of a wavefront fall in different LDS banks.
+constexpr int kSqRow = 17;
+constexpr int kSqFloats = kEncVecsPerWave * 16 * kSqRow;  // per wavefront
+
 // Encodes the vector whose 16-lane group holds x (lane g: dims 16 g ..); returns the fp32 norm and
-// the lane's two words (2 g and 2 g + 1).
-__device__ __forceinline__ float encode16(const float x[16], const float thr[15], int lane, u32x2 &words) {
+// the lane's two words (2 g and 2 g + 1).  sq: this lane group's 16 x 17 floats of LDS.
+__device__ __forceinline__ float encode16(const float x[16], const float thr[15], int lane, float *sq, u32x2 &words) {
 #pragma clang fp contract(off)
     const int g = lane & 15;
-    // ---- squared norm.  Strides 128, 64, 32, 16 pair lane g with g ^ 8, 4, 2, 1 (element e with
-    // itself); both lanes of a pair form s[i] + s[i + stride], as the tree does for i < stride.
-    // Then strides 8, 4, 2, 1 inside the lane.
-    float s[16];
+    // ---- squared norm.  The tree's strides 128, 64, 32, 16 pair dim 16 g + e with the same e in
+    // lanes g ^ 8, 4, 2, 1, and strides 8 .. 1 pair elements inside a lane.  The squares go through
+    // LDS transposed (lane g then holds the squares of element g from all 16 lanes, in lane order),
+    // so strides 128 .. 16 become additions inside the lane and strides 8 .. 1 four exchanges of one
+    // value: the same pairs in the same order as the tree.
+    {
+        float s[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = x[e] * x[e];
-    norm_cross16<8>(s, lane);
-    norm_cross16<4>(s, lane);
-    norm_cross16<2>(s, lane);
-    norm_cross16<1>(s, lane);
+        for (int e = 0; e < 16; ++e) s[e] = x[e] * x[e];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sq[g * kSqRow + e] = s[e];
+    }
+    __builtin_amdgcn_wave_barrier();
+    float ts[16];
+#pragma unroll
+    for (int l = 0; l < 16; ++l) ts[l] = sq[l * kSqRow + g];  // square of dim 16 l + g
 #pragma unroll
     for (int st = 8; st >= 1; st >>= 1)
 #pragma unroll
-        for (int e = 0; e < st; ++e) s[e] = s[e] + s[e + st];
-    const float n32 = __builtin_sqrtf(s[0]);  // correctly rounded in LLVM's AMDGPU lowering
+        for (int l = 0; l < st; ++l) ts[l] = ts[l] + ts[l + st];
+    float s0 = ts[0];  // strides 128 .. 16 done for element g; strides 8 .. 1 pair lanes
+    s0 = s0 + row_xor<8>(s0, lane);
+    s0 = s0 + row_xor<4>(s0, lane);
+    s0 = s0 + row_xor<2>(s0, lane);
+    s0 = s0 + row_xor<1>(s0, lane);
+    const float n32 = __builtin_sqrtf(s0);  // correctly rounded in LLVM's AMDGPU lowering
 
     // ---- y = H x: stages 1, 2, 4, 8 in registers, then 16 .. 128 across lanes (lower lane of a
     // pair: lo + hi; upper lane: lo - hi = lo + (-hi))
@@ -170,8 +178,10 @@ __device__ __forceinline__ float encode16(const float x[16], const float thr[15]
 // are requested before the current group is encoded.  Records are written through buffer
 // resources that cover exactly one record (or nothing for a slot outside the pool or a vector past
 // the end): one store per lane group, in which only that group's lanes have an in-range offset.
+// Five wavefronts per SIMD (at most 96 registers each; the fp32 instance keeps one loop-invariant
+// value in scratch): measured faster than four without the cap.
 template <bool BF16>
-__global__ __launch_bounds__(kEncWaves * kWave) void tq4_encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_eu(5, 5))) void tq4_encode_kernel(EncodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, g = lane & 15;
     const int group0 = static_cast<int>(blockIdx.x) * kEncWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -181,6 +191,8 @@ __global__ __launch_bounds__(kEncWaves * kWave) void tq4_encode_kernel(EncodeArg
     const int total = per_half * ((a.p.src[0] != nullptr) + (a.p.src[1] != nullptr));
     const int n_groups = (total + kEncVecsPerWave - 1) / kEncVecsPerWave;
     if (group0 >= n_groups) return;
+    __shared__ float sq_all[kEncWaves * kSqFloats];
+    float *const sq = sq_all + (threadIdx.x >> 6) * kSqFloats + q * 16 * kSqRow;
     constexpr size_t esize = BF16 ? 2 : 4;
     auto half_of = [&](int vec) { return first_half + static_cast<int>(vec >= per_half); };
     auto rem_of = [&](int vec) { return vec - (vec >= per_half ? per_half : 0); };
@@ -194,7 +206,7 @@ __global__ __launch_bounds__(kEncWaves * kWave) void tq4_encode_kernel(EncodeArg
     };
     auto encode_store = [&](int G, const float x[16], int slot, bool live_group) {
         u32x2 words;
-        const float n32 = encode16(x, a.thr, lane, words);
+        const float n32 = encode16(x, a.thr, lane, sq, words);
         const uint16_t n16 = f32_to_f16_bits(n32);
 #pragma unroll
         for (int qq = 0; qq < kEncVecsPerWave; ++qq) {
