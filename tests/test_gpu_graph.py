@@ -58,8 +58,9 @@ def test_decode_append_step_graph_replays_match_eager():
 
 
 def test_other_entry_points_graph_replays_match_eager():
-    """Verify, prefill, the unfused pair and the INT8 encode, decode and decode-with-append captured
-    in one graph: every replay equals the eager results bit for bit."""
+    """Verify, prefill, the unfused pair, the decode variants, decode without a workspace and the INT8
+    encode, decode and decode-with-append captured in one graph: every replay equals the eager
+    results bit for bit."""
     import torch
     import compressed_kv_attention_kvexec_amd as tq4
     from _pools import int8_to_device, oracle_int8_pool
@@ -99,6 +100,11 @@ def test_other_entry_points_graph_replays_match_eager():
     out_s = torch.empty_like(qd)
     out_a = torch.empty_like(qd)
     ws_a = tq4.new_workspace(tq4.tq4_int8_attn_decode_workspace_size(2, 2000, 24, 4, 64))
+    ws_r = tq4.new_workspace(tq4.tq4_attn_decode_workspace_size(2, 2000, 24, 4, 64))
+    ws_l = tq4.new_workspace(tq4.tq4_attn_decode_workspace_size(2, 2000, 24, 4, 64))
+    out_r = torch.empty_like(qd)
+    out_l = torch.empty_like(qd)
+    out_n = torch.empty_like(qd)
     k_dense = torch.zeros((2, w.n_kv, 2000, 256), dtype=torch.bfloat16, device="cuda")
     v_dense = torch.zeros_like(k_dense)
     calls = [
@@ -106,6 +112,9 @@ def test_other_entry_points_graph_replays_match_eager():
         tq4.prepare_prefill(dppool, qp, ptab, 900, synth.SCALE, out_p, ws_p, s),
         tq4.prepare_reconstruct(dpool, tab, seq, 2000, k_dense, v_dense, s),
         tq4.prepare_sdpa_decode(qd, k_dense, v_dense, seq, synth.SCALE, out_s, ws_s, s),
+        tq4.prepare_decode_variant(dpool, qd, tab, seq, 2000, synth.SCALE, "valu_rotated", out_r, ws_r, s),
+        tq4.prepare_decode_variant(dpool, qd, tab, seq, 2000, synth.SCALE, "valu_literal", out_l, ws_l, s),
+        lambda: tq4.tq4_attn_decode_noalloc(dpool, qd, tab, seq, 2000, synth.SCALE, out_n, stream=s),
     ]
 
     def int8_calls():
@@ -121,7 +130,8 @@ def test_other_entry_points_graph_replays_match_eager():
             c()
         int8_calls()
     torch.cuda.synchronize()
-    ref = [o.clone() for o in (out_v, out_p, out_s, out_d, out_a)]
+    outs = (out_v, out_p, out_s, out_d, out_a, out_r, out_l, out_n)
+    ref = [o.clone() for o in outs]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for c in calls:
@@ -129,13 +139,13 @@ def test_other_entry_points_graph_replays_match_eager():
         int8_calls()
     x = torch.randn(512, 512, device="cuda")
     for rep in range(4):
-        for o in (out_v, out_p, out_s, out_d, out_a):
+        for o in outs:
             o.fill_(0)
         y = x @ x
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, o, r in zip(("verify", "prefill", "sdpa", "int8", "int8 append"),
-                              (out_v, out_p, out_s, out_d, out_a), ref):
+        for name, o, r in zip(("verify", "prefill", "sdpa", "int8", "int8 append", "valu rotated", "valu literal",
+                               "noalloc"), outs, ref):
             assert torch.equal(o, r), f"replay {rep}: {name}"
         assert torch.isfinite(y).all()
