@@ -25,7 +25,9 @@
 //      (O, max, sum) per row and split goes to the workspace.  A wavefront's
 //      decode of the next tile runs inside its work on the current one (table
 //      reads issued during the score products, image writes before the value
-//      products), so the decode's LDS round trip overlaps matrix work;
+//      products), so the decode's LDS round trip overlaps matrix work; a tile's
+//      V words are fetched once per workgroup (16-byte loads into an LDS word
+//      buffer) instead of eight 4-byte gathers per lane in every wavefront;
 //   3. combine: one wavefront per row: merges the splits, inverse rotation,
 //      bf16 output (the same kernel without the rotation serves the INT8 arm).
 #include <cfloat>
@@ -136,12 +138,14 @@ __device__ __forceinline__ void nibble_transpose_pair(const uint32_t in[8], uint
 // 65536, the images' norms (K norms of keys 0..31, then V norms) and the wavefront maxima.  With the
 // table at 2^16, a lane's table address is (index byte) * 256 + 4 * lane + 2^16, which one v_perm
 // builds from the index word and lane_hi = 4 * lane + 2^16 (no base to add).
+constexpr int kPfVRow = 36;  // words per key in the V word buffer (32 + 4 of padding)
 template <int NW>
 struct PfShared {
     PfTileImage img[2];
     uint32_t lut[kLutWords];
     float nrm[2][64];
     float nmax[NW];
+    uint32_t vbuf[2][kTile * kPfVRow];  // V words of a tile, [key][word], for the decode share
 };
 constexpr uint32_t kPfLutOffset = 65536;
 
@@ -189,13 +193,12 @@ void tq4_prefill_kernel(PrefillArgs a) {
     // ---- this wave's share of each tile: K operands e0 .. e0 + E - 1 and V operands
     // 16 + e0 .. 16 + e0 + E - 1, e0 = E * wave.  K operand mt * 8 + 4 h + j is word 16 h + 4 gq + j
     // of key 16 mt + n (E consecutive words, one load); V operand c * 8 + i comes from transposing
-    // word 2 n + c of keys sigma(0..7) (the waves with the same c share the transpose); one norm
-    // per lane (K norms in lanes 0..31, V in 32..63).
+    // word 2 n + c of keys sigma(0..7), read from the workgroup's V word buffer; one norm per lane
+    // (K norms in lanes 0..31, V in 32..63).
     const int e0 = E * wave_u;
     const int mt_w = e0 >> 3, h_w = (e0 >> 2) & 1, j_w = e0 & 3, i_w = e0 & 7;
     const uint32_t k_lane_off = static_cast<uint32_t>(n) * 128u + static_cast<uint32_t>(gq) * 16u +
                                 2048u * mt_w + 64u * h_w + 4u * j_w;
-    const uint32_t v_lane_off = static_cast<uint32_t>(gq) * 512u + static_cast<uint32_t>(n) * 8u + 4u * mt_w;
     // transpose selectors of this wave's row pairs i_w / 2 .. (i_w + E) / 2 - 1 (all in one half)
     const uint32_t half_sel = (i_w >> 2) ? 0x07060302u : 0x05040100u;
     uint32_t pair_sel[E / 2];
@@ -206,32 +209,41 @@ void tq4_prefill_kernel(PrefillArgs a) {
     using KWords = std::conditional_t<E == 4, u32x4, u32x2>;
     struct Staging {
         KWords k;
-        uint32_t v[8];
         uint32_t n;
         bool valid;
     };
+    // The V words of a tile are fetched once per workgroup: waves 0..3 load 16 bytes per lane (keys
+    // 8 w .. 8 w + 7) into vtmp and store them into an LDS word buffer one step later; the decode
+    // share reads its eight words per lane from there.
+    const bool v_loader = wave_u < kTile / 8;
+    u32x4 vtmp;
+    const uint32_t v_key = static_cast<uint32_t>(wave_u * 8 + (lane >> 3)), v_chunk = static_cast<uint32_t>(lane & 7);
     // page index of a key (wave-uniform; a shift for power-of-two pages)
     auto page_of = [&](int key) { return a.page_shift >= 0 ? key >> a.page_shift : key / p.page_size; };
     auto fetch_pid = [&](int t) {  // wave-uniform address: a scalar load
         return pt[min(page_of(key_begin + t * kTile), pt_last)];
     };
-    auto load_tile = [&](Staging &st, int t, int pid) {
+    // loads this wave's K share and norm of tile t; returns the tile's first record
+    auto load_tile = [&](Staging &st, int t, int pid) -> int64_t {
         const int key0 = key_begin + t * kTile;  // t is clamped by the caller to a tile of this split
         const int off0 = key0 - page_of(key0) * p.page_size;
         st.valid = pid >= 0 && pid < p.num_pages;  // page IDs outside the pool read page 0, masked
         const int64_t rec = (static_cast<int64_t>(st.valid ? pid : 0) * p.n_kv + g) * p.page_size + off0;
         const char *kb = reinterpret_cast<const char *>(p.k_words) + rec * (kWords * 4);
-        const char *vb = reinterpret_cast<const char *>(p.v_words) + rec * (kWords * 4);
         st.k = *reinterpret_cast<const KWords *>(kb + k_lane_off);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t koff = (j < 4) ? 128u * j : 2048u + 128u * (j - 4);
-            st.v[j] = *reinterpret_cast<const uint32_t *>(vb + v_lane_off + koff);
-        }
         const uint16_t *nb = (lane < 32 ? p.k_norms : p.v_norms) + rec + (lane & 31);
         st.n = *nb;
+        return rec;
     };
-    auto load_share = [&](Staging &st, int t) { load_tile(st, t, fetch_pid(t)); };
+    auto load_v = [&](int64_t rec) {
+        if (v_loader)
+            vtmp = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(p.v_words) +
+                                                    (rec + v_key) * (kWords * 4) + 16u * v_chunk);
+    };
+    auto store_v = [&](int vb) {
+        if (v_loader) *reinterpret_cast<u32x4 *>(&sh.vbuf[vb][v_key * kPfVRow + 4 * v_chunk]) = vtmp;
+    };
+    auto load_share = [&](Staging &st, int t) { return load_tile(st, t, fetch_pid(t)); };
     const char *lds = reinterpret_cast<const char *>(&sh);
     const uint32_t lane_hi = static_cast<uint32_t>(lane) * 4u + kPfLutOffset;
     // A wave's share of a tile's decode in two parts: the table reads (issued while the matrix
@@ -240,12 +252,19 @@ void tq4_prefill_kernel(PrefillArgs a) {
         half8 d[2 * E];
         float nrm;
     };
-    auto decode_issue = [&](const Staging &st, Decoded &dc) {
+    auto decode_issue = [&](const Staging &st, Decoded &dc, int vb) {
+        // word 2 n + c of keys sigma(0..7) from the V word buffer
+        uint32_t vw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int key = (j < 4) ? 4 * gq + j : 16 + 4 * gq + (j - 4);
+            vw[j] = sh.vbuf[vb][key * kPfVRow + 2 * n + mt_w];
+        }
 #pragma unroll
         for (int j = 0; j < E; ++j) dc.d[j] = pf_lut_decode(st.k[j], lane_hi, lds);
         uint32_t uw[E];  // rows i_w .. i_w + E - 1 of the transposed words
 #pragma unroll
-        for (int i = 0; i < E; i += 2) nibble_transpose_pair(st.v, half_sel, pair_sel[i / 2], uw[i], uw[i + 1]);
+        for (int i = 0; i < E; i += 2) nibble_transpose_pair(vw, half_sel, pair_sel[i / 2], uw[i], uw[i + 1]);
 #pragma unroll
         for (int i = 0; i < E; ++i) dc.d[E + i] = pf_lut_decode(uw[i], lane_hi, lds);
         dc.nrm = f16_bits_to_f32(static_cast<uint16_t>(st.n));
@@ -258,16 +277,16 @@ void tq4_prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < E; ++i) im.op[16 + e0 + i][lane] = dc.d[E + i];
         sh.nrm[b][lane] = dc.nrm;  // every wave writes the same values
     };
-    auto decode_share = [&](const Staging &st, int b) {
+    auto decode_share = [&](const Staging &st, int b, int vb) {
         Decoded dc;
-        decode_issue(st, dc);
+        decode_issue(st, dc, vb);
         __builtin_amdgcn_sched_barrier(0);
         decode_write(dc, b);
     };
 
     // two staging sets, each refilled in place two tiles ahead of its decode
     Staging sa, sb;
-    load_share(sa, 0);
+    load_v(load_share(sa, 0));
 
     // ---- per-block row data: causal limit, score factor, query operand (rows past the chunk see
     // no key and are never written)
@@ -329,6 +348,7 @@ void tq4_prefill_kernel(PrefillArgs a) {
         if (lane == 0) nmax_sh[wave_u] = nmx;
     }
     build_lut<NT>(lut_mem, a.lut_pairs, tid);
+    store_v(0);  // tile 0's V words
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) nmx = fmaxf(nmx, nmax_sh[w]);
@@ -339,10 +359,11 @@ void tq4_prefill_kernel(PrefillArgs a) {
         eo = nmx <= 65504.f ? E - 7 : kPfNormExpMax;
     }
     const int t_last = max(n_tiles - 1, 0);
-    decode_share(sa, 0);
+    decode_share(sa, 0, 0);
     bool valid0 = sa.valid, valid1 = false;  // tiles in img[0] and img[1]
-    load_share(sb, min(1, t_last));
-    load_share(sa, min(2, t_last));
+    load_v(load_share(sb, min(1, t_last)));
+    store_v(1);  // tile 1's V words (waits for them here, once)
+    load_v(load_share(sa, min(2, t_last)));
     __syncthreads();
 
     float4v oacc[R][16];
@@ -482,10 +503,15 @@ void tq4_prefill_kernel(PrefillArgs a) {
         const bool vcmp = (b_cmp ? valid1 : valid0) && t < n_tiles;
         const int tn = min(t_next, t_last);
         const int pid_next = fetch_pid(tn);  // requested now, used after the softmax
-        compute(b_cmp, t, vcmp, [&] { decode_issue(st, dc); }, [&] {
+        compute(b_cmp, t, vcmp, [&] { decode_issue(st, dc, (t + 1) & 1); }, [&] {
             decode_write(dc, b_dec);
             vdec = st.valid;
-            load_tile(st, tn, pid_next);  // the staging set is free again: refill it before the value products
+            // the staging set is free again: refill it with tile t + 3 before the value products;
+            // tile t + 2's V words go to their buffer (its last reader was tile t's decode, one
+            // barrier ago) and tile t + 3's are requested
+            const int64_t rec = load_tile(st, tn, pid_next);
+            store_v((t + 2) & 1);
+            load_v(rec);
         });
         __syncthreads();
     };
