@@ -14,20 +14,44 @@
 // records are bit-identical to it.
 #pragma clang fp contract(off)
 
+#include <cfloat>
+
 #include "tq4_device.h"
 #include "tq4_encode_wave.h"
 #include "tq4_launch.h"
 
 namespace tq4 {
 
+// Division by a fixed d in [1, 2^31) of x in [0, 2^31): q = (umulhi(x, m) + x) >> l with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (Granlund and Montgomery, "Division by
+// Invariant Integers using Multiplication", unsigned division); umulhi(x, m) + x stays below 2^32.
+struct FastDiv {
+    uint32_t m;
+    uint32_t l;
+};
+
+inline FastDiv make_fast_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t{1} << l) < d) ++l;
+    const uint64_t m = ((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1;
+    return FastDiv{static_cast<uint32_t>(m), l};
+}
+
+__device__ __forceinline__ int fast_div(int x, FastDiv f) {
+    const uint32_t ux = static_cast<uint32_t>(x);
+    return static_cast<int>((__umulhi(ux, f.m) + ux) >> f.l);
+}
+
 struct EncodeArgs {
     EncodeParams p;
     float thr[15];
+    FastDiv by_kv;    // n_kv
+    FastDiv by_page;  // page_size
 };
 
 constexpr int kEncWaves = 4;                 // wavefronts per workgroup
 constexpr int kEncVecsPerWave = 4;           // one vector per 16-lane group
-constexpr int64_t kEncMaxWorkgroups = 2048;  // 8 per CU (all resident): each wavefront loops
+constexpr int64_t kEncMaxWorkgroups = 2048;  // 8 per CU, 6 resident at a time; each wavefront loops
 constexpr int kEncDropOffset = 0x40000000;   // a buffer offset past any record: the store is dropped
 constexpr int kBufferFlags = 0x00020000;     // raw 32-bit buffer resource word 3
 
@@ -95,6 +119,34 @@ __device__ __forceinline__ void hadamard_cross16(float y[16], int lane) {
 constexpr int kSqRow = 17;
 constexpr int kSqFloats = kEncVecsPerWave * 16 * kSqRow;  // per wavefront
 
+// 2 w + (bit of this lane in mask m), one v_addc_co_u32 with the mask as carry in.
+__device__ __forceinline__ uint32_t add_twice_carry(uint32_t w, uint64_t m) {
+    uint32_t r;
+    uint64_t carry_out;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
+    return r;
+}
+
+// w = 16 w + idx(v): the 4-bit index of coordinate v goes into the word one bit at a time (see the
+// index comment in encode16); tb_j = 2 bits(t_j).
+__device__ __forceinline__ uint32_t index_bits(uint32_t w, float v, uint32_t tb0, uint32_t tb1, uint32_t tb2,
+                                               uint32_t tb3, uint32_t tb4, uint32_t tb5, uint32_t tb6) {
+    const uint32_t yb = __builtin_bit_cast(uint32_t, v);
+    const uint64_t mp = __builtin_amdgcn_ballot_w64(v > 0.0f);
+    const uint32_t key = add_twice_carry(yb, ~mp);
+    const bool c4 = key > tb3;
+    const bool c2 = key > (c4 ? tb5 : tb1);
+    const uint32_t hi = c2 ? tb6 : tb4, lo = c2 ? tb2 : tb0;
+    const bool c1 = key > (c4 ? hi : lo);
+    const uint64_t m4 = __builtin_amdgcn_ballot_w64(c4);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(c2);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(c1);
+    w = add_twice_carry(w, mp);
+    w = add_twice_carry(w, ~(m4 ^ mp));
+    w = add_twice_carry(w, ~(m2 ^ mp));
+    return add_twice_carry(w, ~(m1 ^ mp));
+}
+
 // Encodes the vector whose 16-lane group holds x (lane g: dims 16 g ..); returns the fp32 norm and
 // the lane's two words (2 g and 2 g + 1).  sq: this lane group's 16 x 17 floats of LDS.
 __device__ __forceinline__ float encode16(const float x[16], const float thr[15], int lane, float *sq, u32x2 &words) {
@@ -146,28 +198,45 @@ __device__ __forceinline__ float encode16(const float x[16], const float thr[15]
     hadamard_cross16<4>(y, lane);
     hadamard_cross16<8>(y, lane);
 
-    // ---- indices.  With a = |y| (or the next float above it for y <= 0) and t_j = b_{8+j}(16 n)
-    // ascending, c = #{ j : a > t_j } by a three-level search (sorted thresholds); idx = 8 + c for
-    // y > 0, else 7 - c (the thresholds are exact negatives of each other, b_7 = 0).
+    // ---- indices: idx = #{ i : y > b_i (16 n) } over the 15 ascending thresholds.
     const float mscale = 16.0f * n32;
-    float t[7];
-#pragma unroll
-    for (int j = 0; j < 7; ++j) t[j] = thr[8 + j] * mscale;
     uint32_t w0 = 0, w1 = 0;
+    if (__all(n32 <= FLT_MAX)) {
+        // Every norm of the wavefront is finite, so n < 2^64 (its square did not overflow) and y and
+        // the thresholds are finite (|y| <= 16 n).  The
+        // thresholds are exact negatives of each other (b_7 = 0), so with c = #{ j : t_j < |y| } for
+        // y > 0 and c = #{ j : t_j <= |y| } otherwise (t_j = b_{8+j} (16 n), j = 0 .. 6), idx is
+        // 8 + c or 7 - c, i.e. bit 3 = [y > 0] and bits 2 .. 0 those of c, each flipped for y <= 0.
+        // Compared as integers: key = 2 bits(y) + [y <= 0] (the doubling drops the sign) against
+        // 2 bits(t_j) orders both cases at once.  c comes from a three-level search; the nibble
+        // goes into the word one bit at a time, w = 2 w + bit, highest element first.
+        const uint32_t tb0 = 2u * __builtin_bit_cast(uint32_t, thr[8] * mscale);
+        const uint32_t tb1 = 2u * __builtin_bit_cast(uint32_t, thr[9] * mscale);
+        const uint32_t tb2 = 2u * __builtin_bit_cast(uint32_t, thr[10] * mscale);
+        const uint32_t tb3 = 2u * __builtin_bit_cast(uint32_t, thr[11] * mscale);
+        const uint32_t tb4 = 2u * __builtin_bit_cast(uint32_t, thr[12] * mscale);
+        const uint32_t tb5 = 2u * __builtin_bit_cast(uint32_t, thr[13] * mscale);
+        const uint32_t tb6 = 2u * __builtin_bit_cast(uint32_t, thr[14] * mscale);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const bool pos = y[e] > 0.0f;
-        const uint32_t abits = __builtin_bit_cast(uint32_t, y[e]) & 0x7fffffffu;
-        const float a = __builtin_bit_cast(float, pos ? abits : abits + 1u);
-        const bool c4 = a > t[3];
-        const bool c2 = a > (c4 ? t[5] : t[1]);
-        const bool c1 = a > (c4 ? (c2 ? t[6] : t[4]) : (c2 ? t[2] : t[0]));
-        const uint32_t c = (c4 ? 4u : 0u) + (c2 ? 2u : 0u) + (c1 ? 1u : 0u);
-        const uint32_t idx = pos ? 8u + c : 7u - c;
-        if (e < 8)
-            w0 |= idx << (4 * e);
-        else
-            w1 |= idx << (4 * (e - 8));
+        for (int e = 7; e >= 0; --e) {
+            w0 = index_bits(w0, y[e], tb0, tb1, tb2, tb3, tb4, tb5, tb6);
+            w1 = index_bits(w1, y[e + 8], tb0, tb1, tb2, tb3, tb4, tb5, tb6);
+        }
+    } else {
+        // an infinite or NaN norm in the wavefront: the count itself, over all 15 thresholds
+        float t[15];
+#pragma unroll
+        for (int i = 0; i < 15; ++i) t[i] = thr[i] * mscale;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            uint32_t idx = 0;
+#pragma unroll
+            for (int i = 0; i < 15; ++i) idx += y[e] > t[i] ? 1u : 0u;
+            if (e < 8)
+                w0 |= idx << (4 * e);
+            else
+                w1 |= idx << (4 * (e - 8));
+        }
     }
     words = u32x2{w0, w1};
     return n32;
@@ -178,16 +247,21 @@ __device__ __forceinline__ float encode16(const float x[16], const float thr[15]
 // are requested before the current group is encoded.  Records are written through buffer
 // resources that cover exactly one record (or nothing for a slot outside the pool or a vector past
 // the end): one store per lane group, in which only that group's lanes have an in-range offset.
-// Five wavefronts per SIMD (at most 96 registers each; the fp32 instance keeps one loop-invariant
-// value in scratch): measured faster than four without the cap.
+// Six wavefronts per SIMD (at most 85 registers each, none spilled): measured faster than five.
+// Divisions by n_kv and page_size are multiplications by host-computed constants.
 template <bool BF16>
-__global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_eu(5, 5))) void tq4_encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_eu(6, 6))) void tq4_encode_kernel(EncodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int q = lane >> 4, g = lane & 15;
     const int group0 = static_cast<int>(blockIdx.x) * kEncWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int stride = static_cast<int>(gridDim.x) * kEncWaves;
     const int per_half = a.p.n_tokens * a.p.n_kv;
     const int first_half = a.p.src[0] != nullptr ? 0 : 1;
+    // the two halves' pointers, read once (an index into the argument array would be a scalar
+    // load and wait at every use)
+    const char *const src0 = static_cast<const char *>(a.p.src[0]), *const src1 = static_cast<const char *>(a.p.src[1]);
+    uint32_t *const words0 = a.p.words[0], *const words1 = a.p.words[1];
+    uint16_t *const norms0 = a.p.norms[0], *const norms1 = a.p.norms[1];
     const int total = per_half * ((a.p.src[0] != nullptr) + (a.p.src[1] != nullptr));
     const int n_groups = (total + kEncVecsPerWave - 1) / kEncVecsPerWave;
     if (group0 >= n_groups) return;
@@ -201,8 +275,8 @@ __global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_
     auto load = [&](int G, float x[16], int &slot) {
         const int vec = vec_of(G);
         const int rem = rem_of(vec);
-        load16<BF16>(static_cast<const char *>(a.p.src[half_of(vec)]) + static_cast<int64_t>(rem) * kDim * esize, g, x);
-        slot = a.p.slots[rem / a.p.n_kv];
+        load16<BF16>((half_of(vec) ? src1 : src0) + static_cast<int64_t>(rem) * kDim * esize, g, x);
+        slot = a.p.slots[fast_div(rem, a.by_kv)];
     };
     auto encode_store = [&](int G, const float x[16], int slot, bool live_group) {
         u32x2 words;
@@ -213,17 +287,18 @@ __global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_
             const int vec = G * kEncVecsPerWave + qq;
             const int vq = min(vec, total - 1);
             const int half = half_of(vq);
-            const int head = rem_of(vq) % a.p.n_kv;
+            const int rq = rem_of(vq);
+            const int head = rq - fast_div(rq, a.by_kv) * a.p.n_kv;
             const int s_u = __builtin_amdgcn_readlane(slot, 16 * qq);
             const bool valid = live_group && vec < total && s_u >= 0 && s_u < a.p.num_slots;
             const int sl = valid ? s_u : 0;
-            const int page = sl / a.p.page_size;
+            const int page = fast_div(sl, a.by_page);
             const int64_t rec =
                 (static_cast<int64_t>(page) * a.p.n_kv + head) * a.p.page_size + (sl - page * a.p.page_size);
             const __amdgpu_buffer_rsrc_t wr =
-                __builtin_amdgcn_make_buffer_rsrc(a.p.words[half] + rec * kWords, 0, valid ? kWords * 4 : 0, kBufferFlags);
+                __builtin_amdgcn_make_buffer_rsrc((half ? words1 : words0) + rec * kWords, 0, valid ? kWords * 4 : 0, kBufferFlags);
             const __amdgpu_buffer_rsrc_t nr =
-                __builtin_amdgcn_make_buffer_rsrc(a.p.norms[half] + rec, 0, valid ? 2 : 0, kBufferFlags);
+                __builtin_amdgcn_make_buffer_rsrc((half ? norms1 : norms0) + rec, 0, valid ? 2 : 0, kBufferFlags);
             const int word_off = q == qq ? 8 * g : kEncDropOffset;
             const int norm_off = (q == qq && g == 0) ? 0 : kEncDropOffset;
             __builtin_amdgcn_raw_buffer_store_b64(words, wr, word_off, 0, 0);
@@ -236,7 +311,7 @@ __global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_
     int slot0, slot1;
     load(group0, x0, slot0);
     {   // dropped stores: the loop is entered with the same pending operations as its back edge
-        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.p.words[half_of(0)], 0, 0, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(half_of(0) ? words1 : words0, 0, 0, kBufferFlags);
 #pragma unroll
         for (int qq = 0; qq < kEncVecsPerWave; ++qq) {
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, kEncDropOffset, 0, 0);
@@ -261,6 +336,8 @@ hipError_t launch_encode(const EncodeParams &p, hipStream_t stream) {
     a.p = p;
     const Codebook &cb = codebook();
     for (int i = 0; i < 15; ++i) a.thr[i] = cb.threshold[i];
+    a.by_kv = make_fast_div(static_cast<uint32_t>(p.n_kv));
+    a.by_page = make_fast_div(static_cast<uint32_t>(p.page_size));
     const int halves = (p.src[0] != nullptr) + (p.src[1] != nullptr);
     const int64_t vectors = static_cast<int64_t>(halves) * p.n_tokens * p.n_kv;
     if (vectors == 0) return hipSuccess;

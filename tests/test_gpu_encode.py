@@ -52,7 +52,8 @@ def test_encode_bf16_source_and_k_only():
 
 
 def test_encode_edge_vectors_and_bad_slots():
-    """Zero, spike, constant, huge, tiny and mixed-scale vectors; out-of-pool slots are skipped."""
+    """Zero, spike, constant, huge, tiny, overflowing and mixed-scale vectors; out-of-pool slots are
+    skipped."""
     w = synth.Workload(90, "edge", "decode", 1, 64, 4, seq_lens=(256,), n_kv=2)
     rng = np.random.default_rng(90)
     n = 40
@@ -65,6 +66,14 @@ def test_encode_edge_vectors_and_bad_slots():
     k[4] *= np.float32(1e-20)
     k[5, 0, :128] *= np.float32(1e4)
     k[6, 1, ::2] = 0.0
+    # the largest finite norms and squares that overflow (infinite norm), squares that underflow,
+    # an infinite element, and a wavefront whose vectors mix finite and infinite norms
+    unit = k / np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)
+    k[9] = (unit[9] * 1.5e19).astype(np.float32)
+    k[10] *= np.float32(1e-30)
+    k[11, 0, 5] = np.inf
+    k[12, 1] *= np.float32(2e18)
+    k[13] = (unit[13] * 2.5e19).astype(np.float32)
     v = -k[::-1].copy()
     slots = rng.permutation(4 * 64)[:n].astype(np.int32)
     ref = oracle.Pool.empty(4, 2, 64)
@@ -87,5 +96,22 @@ def test_encode_bit_exact_large_sample():
     k = synth.kv_source(w, 0, len(slots), synth.T_K)
     v = synth.kv_source(w, 0, len(slots), synth.T_V)
     ref = oracle.Pool.empty(w.pool_pages, w.n_kv, w.page_size)
+    oracle.encode_to_pool(ref, k, v, slots)
+    _assert_pools_equal(_gpu_encode(w, k, v, slots), ref)
+
+
+@pytest.mark.parametrize("n_kv,page", [(1, 32), (3, 96), (5, 160), (6, 64), (8, 1024)])
+def test_encode_head_counts_and_page_sizes(n_kv, page):
+    """Head counts and page sizes that are not powers of two: the slot -> (page, offset) and
+    vector -> (token, head) divisions."""
+    pages = 2048 // page + 3
+    w = synth.Workload(91, "shapes", "decode", 1, page, pages, seq_lens=(64,), n_kv=n_kv)
+    rng = np.random.default_rng(91 + n_kv)
+    n = 257
+    k = rng.standard_normal((n, n_kv, 256)).astype(np.float32)
+    v = rng.standard_normal((n, n_kv, 256)).astype(np.float32) * np.float32(3.0)
+    slots = rng.permutation(pages * page)[:n].astype(np.int32)
+    slots[0] = pages * page - 1  # the pool's last slot
+    ref = oracle.Pool.empty(pages, n_kv, page)
     oracle.encode_to_pool(ref, k, v, slots)
     _assert_pools_equal(_gpu_encode(w, k, v, slots), ref)
