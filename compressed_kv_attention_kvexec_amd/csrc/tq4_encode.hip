@@ -52,8 +52,6 @@ struct EncodeArgs {
 constexpr int kEncWaves = 4;                 // wavefronts per workgroup
 constexpr int kEncVecsPerWave = 4;           // one vector per 16-lane group
 constexpr int64_t kEncMaxWorkgroups = 2048;  // 8 per CU, 6 resident at a time; each wavefront loops
-constexpr int kEncDropOffset = 0x40000000;   // a buffer offset past any record: the store is dropped
-constexpr int kBufferFlags = 0x00020000;     // raw 32-bit buffer resource word 3
 
 // Lane g's 16 source values (dims 16 g .. 16 g + 15) of one 256-dim fp32 or bf16 vector.
 template <bool BF16>
@@ -244,9 +242,9 @@ __device__ __forceinline__ float encode16(const float x[16], const float thr[15]
 
 // Each wavefront encodes groups of four vectors, group0, group0 + stride, ... (vectors in [half]
 // [token][kv head] order, lane group q takes vector 4 G + q).  The next group's sources and slots
-// are requested before the current group is encoded.  Records are written through buffer
-// resources that cover exactly one record (or nothing for a slot outside the pool or a vector past
-// the end): one store per lane group, in which only that group's lanes have an in-range offset.
+// are requested before the current group is encoded.  Each lane computes its vector's record
+// address itself and the wavefront writes the four records with one 8-byte store per lane and one
+// norm store (lanes with g = 0); a slot outside the pool or a vector past the end is not written.
 // Six wavefronts per SIMD (at most 85 registers each, none spilled): measured faster than five.
 // Divisions by n_kv and page_size are multiplications by host-computed constants.
 template <bool BF16>
@@ -282,27 +280,19 @@ __global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_
         u32x2 words;
         const float n32 = encode16(x, a.thr, lane, sq, words);
         const uint16_t n16 = f32_to_f16_bits(n32);
-#pragma unroll
-        for (int qq = 0; qq < kEncVecsPerWave; ++qq) {
-            const int vec = G * kEncVecsPerWave + qq;
-            const int vq = min(vec, total - 1);
-            const int half = half_of(vq);
-            const int rq = rem_of(vq);
-            const int head = rq - fast_div(rq, a.by_kv) * a.p.n_kv;
-            const int s_u = __builtin_amdgcn_readlane(slot, 16 * qq);
-            const bool valid = live_group && vec < total && s_u >= 0 && s_u < a.p.num_slots;
-            const int sl = valid ? s_u : 0;
-            const int page = fast_div(sl, a.by_page);
-            const int64_t rec =
-                (static_cast<int64_t>(page) * a.p.n_kv + head) * a.p.page_size + (sl - page * a.p.page_size);
-            const __amdgpu_buffer_rsrc_t wr =
-                __builtin_amdgcn_make_buffer_rsrc((half ? words1 : words0) + rec * kWords, 0, valid ? kWords * 4 : 0, kBufferFlags);
-            const __amdgpu_buffer_rsrc_t nr =
-                __builtin_amdgcn_make_buffer_rsrc((half ? norms1 : norms0) + rec, 0, valid ? 2 : 0, kBufferFlags);
-            const int word_off = q == qq ? 8 * g : kEncDropOffset;
-            const int norm_off = (q == qq && g == 0) ? 0 : kEncDropOffset;
-            __builtin_amdgcn_raw_buffer_store_b64(words, wr, word_off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16(n16, nr, norm_off, 0, 0);
+        // each lane group stores its own vector's record: lane g writes words 2 g, 2 g + 1 (< 2^31
+        // records, so the record index is a 32-bit value)
+        const int vec = G * kEncVecsPerWave + q;
+        const int vq = min(vec, total - 1);
+        const int half = half_of(vq);
+        const int rq = rem_of(vq);
+        const int head = rq - fast_div(rq, a.by_kv) * a.p.n_kv;
+        const bool valid = live_group && vec < total && slot >= 0 && slot < a.p.num_slots;
+        if (valid) {
+            const int page = fast_div(slot, a.by_page);
+            const uint32_t rec = static_cast<uint32_t>((page * a.p.n_kv + head) * a.p.page_size + (slot - page * a.p.page_size));
+            *reinterpret_cast<u32x2 *>((half ? words1 : words0) + static_cast<uint64_t>(rec) * kWords + 2 * g) = words;
+            if (g == 0) (half ? norms1 : norms0)[rec] = n16;
         }
     };
 
@@ -310,14 +300,6 @@ __global__ __launch_bounds__(kEncWaves * kWave) __attribute__((amdgpu_waves_per_
     float x0[16], x1[16];
     int slot0, slot1;
     load(group0, x0, slot0);
-    {   // dropped stores: the loop is entered with the same pending operations as its back edge
-        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(half_of(0) ? words1 : words0, 0, 0, kBufferFlags);
-#pragma unroll
-        for (int qq = 0; qq < kEncVecsPerWave; ++qq) {
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, none, kEncDropOffset, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(0), none, kEncDropOffset, 0, 0);
-        }
-    }
     for (int G = group0; G < n_groups; G += 2 * stride) {
         const bool live1 = G < n_groups - stride;
         const int G1 = live1 ? G + stride : G;
