@@ -852,6 +852,8 @@ def main() -> int:
         print(json.dumps({"int8": int8_leg(args.workload, dev)}), flush=True)
         return 0
     if args.only_encode:  # the encoder alone, for profiler runs
+        if args.calibrate_copy_mib > 0:
+            calibration_copy(args.calibrate_copy_mib, dev)
         w = synth.WORKLOADS[args.workload]
         pool = tq4.Tq4LayerPool.empty(w.pool_pages, w.n_kv, w.page_size, device=dev)
         print(json.dumps({"encode": encode_leg({"pool": pool}, w, dev)}), flush=True)
