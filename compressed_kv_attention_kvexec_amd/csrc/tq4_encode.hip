@@ -22,26 +22,6 @@
 
 namespace tq4 {
 
-// Division by a fixed d in [1, 2^31) of x in [0, 2^31): q = (umulhi(x, m) + x) >> l with
-// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (Granlund and Montgomery, "Division by
-// Invariant Integers using Multiplication", unsigned division); umulhi(x, m) + x stays below 2^32.
-struct FastDiv {
-    uint32_t m;
-    uint32_t l;
-};
-
-inline FastDiv make_fast_div(uint32_t d) {
-    uint32_t l = 0;
-    while ((uint64_t{1} << l) < d) ++l;
-    const uint64_t m = ((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1;
-    return FastDiv{static_cast<uint32_t>(m), l};
-}
-
-__device__ __forceinline__ int fast_div(int x, FastDiv f) {
-    const uint32_t ux = static_cast<uint32_t>(x);
-    return static_cast<int>((__umulhi(ux, f.m) + ux) >> f.l);
-}
-
 struct EncodeArgs {
     EncodeParams p;
     float thr[15];

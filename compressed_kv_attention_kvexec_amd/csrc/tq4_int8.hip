@@ -45,6 +45,8 @@ constexpr int kI8BufferFlags = 0x00020000;
 
 struct Int8EncodeArgs {
     Int8EncodeParams p;
+    FastDiv by_kv;    // n_kv
+    FastDiv by_page;  // page_size
 };
 
 __device__ __forceinline__ float wave_max_abs(const float x[4]) {
@@ -82,30 +84,35 @@ __global__ __launch_bounds__(kI8EncWaves * kWave) void tq4_int8_encode_kernel(In
     const int first_half = a.p.src[0] != nullptr ? 0 : 1;
     const int total = per_half * ((a.p.src[0] != nullptr) + (a.p.src[1] != nullptr));
     if (wave0 >= total) return;
+    // the two halves' pointers, read once (an index into the argument array would be a scalar
+    // load and wait at every use)
+    const char *const src0 = static_cast<const char *>(a.p.src[0]), *const src1 = static_cast<const char *>(a.p.src[1]);
+    int8_t *const codes0 = a.p.codes[0], *const codes1 = a.p.codes[1];
+    uint16_t *const scales0 = a.p.scales[0], *const scales1 = a.p.scales[1];
     constexpr size_t esize = BF16 ? 2 : 4;
     auto half_of = [&](int vec) { return first_half + static_cast<int>(vec >= per_half); };
     auto rem_of = [&](int vec) { return vec - (vec >= per_half ? per_half : 0); };
     auto load = [&](int vec, float x[4], int &slot) {
         const int rem = rem_of(vec);
-        encode_load(static_cast<const char *>(a.p.src[half_of(vec)]) + static_cast<int64_t>(rem) * kDim * esize, BF16,
-                    lane, x);
-        slot = a.p.slots[rem / a.p.n_kv];
+        encode_load((half_of(vec) ? src1 : src0) + static_cast<int64_t>(rem) * kDim * esize, BF16, lane, x);
+        slot = a.p.slots[fast_div(rem, a.by_kv)];
     };
     const int scale_off = lane == 0 ? 0 : kI8DropOffset;
     auto encode_store = [&](int vec, const float x[4], int slot, bool live) {
         const int half = half_of(vec);
-        const int head = rem_of(vec) % a.p.n_kv;
+        const int rv = rem_of(vec);
+        const int head = rv - fast_div(rv, a.by_kv) * a.p.n_kv;
         const int s_u = __builtin_amdgcn_readfirstlane(slot);
         const bool valid = live && s_u >= 0 && s_u < a.p.num_slots;
         const int sl = valid ? s_u : 0;
-        const int page = sl / a.p.page_size;
+        const int page = fast_div(sl, a.by_page);
         const int64_t rec = (static_cast<int64_t>(page) * a.p.n_kv + head) * a.p.page_size + (sl - page * a.p.page_size);
         uint16_t s16;
         const uint32_t word = int8_encode_lane(x, s16);
         const __amdgpu_buffer_rsrc_t cr =
-            __builtin_amdgcn_make_buffer_rsrc(a.p.codes[half] + rec * kDim, 0, valid ? kDim : 0, kI8BufferFlags);
+            __builtin_amdgcn_make_buffer_rsrc((half ? codes1 : codes0) + rec * kDim, 0, valid ? kDim : 0, kI8BufferFlags);
         const __amdgpu_buffer_rsrc_t sr =
-            __builtin_amdgcn_make_buffer_rsrc(a.p.scales[half] + rec, 0, valid ? 2 : 0, kI8BufferFlags);
+            __builtin_amdgcn_make_buffer_rsrc((half ? scales1 : scales0) + rec, 0, valid ? 2 : 0, kI8BufferFlags);
         __builtin_amdgcn_raw_buffer_store_b32(word, cr, 4 * lane, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b16(s16, sr, scale_off, 0, 0);
     };
@@ -128,6 +135,8 @@ __global__ __launch_bounds__(kI8EncWaves * kWave) void tq4_int8_encode_kernel(In
 hipError_t launch_int8_encode(const Int8EncodeParams &p, hipStream_t stream) {
     Int8EncodeArgs a;
     a.p = p;
+    a.by_kv = make_fast_div(static_cast<uint32_t>(p.n_kv));
+    a.by_page = make_fast_div(static_cast<uint32_t>(p.page_size));
     const int halves = (p.src[0] != nullptr) + (p.src[1] != nullptr);
     const int64_t vectors = static_cast<int64_t>(halves) * p.n_tokens * p.n_kv;
     if (vectors == 0) return hipSuccess;
