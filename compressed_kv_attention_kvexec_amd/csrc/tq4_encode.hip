@@ -97,11 +97,17 @@ __device__ __forceinline__ void hadamard_cross16(float y[16], int lane) {
 constexpr int kSqRow = 17;
 constexpr int kSqFloats = kEncVecsPerWave * 16 * kSqRow;  // per wavefront
 
-// 2 w + (bit of this lane in mask m), one v_addc_co_u32 with the mask as carry in.
+// 2 w + (bit of this lane in mask m), one v_addc_co_u32 with the mask as carry in.  A mask that a
+// vector compare has just written needs two wait states before a vector instruction reads it, which
+// the compiler does not check inside inline assembly: kFromCompare puts them in front.
+template <bool kFromCompare>
 __device__ __forceinline__ uint32_t add_twice_carry(uint32_t w, uint64_t m) {
     uint32_t r;
     uint64_t carry_out;
-    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
+    if constexpr (kFromCompare)
+        asm("s_nop 1\n\tv_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
+    else
+        asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
     return r;
 }
 
@@ -111,7 +117,7 @@ __device__ __forceinline__ uint32_t index_bits(uint32_t w, float v, uint32_t tb0
                                                uint32_t tb3, uint32_t tb4, uint32_t tb5, uint32_t tb6) {
     const uint32_t yb = __builtin_bit_cast(uint32_t, v);
     const uint64_t mp = __builtin_amdgcn_ballot_w64(v > 0.0f);
-    const uint32_t key = add_twice_carry(yb, ~mp);
+    const uint32_t key = add_twice_carry<false>(yb, ~mp);  // ~mp: a scalar instruction's result
     const bool c4 = key > tb3;
     const bool c2 = key > (c4 ? tb5 : tb1);
     const uint32_t hi = c2 ? tb6 : tb4, lo = c2 ? tb2 : tb0;
@@ -119,10 +125,10 @@ __device__ __forceinline__ uint32_t index_bits(uint32_t w, float v, uint32_t tb0
     const uint64_t m4 = __builtin_amdgcn_ballot_w64(c4);
     const uint64_t m2 = __builtin_amdgcn_ballot_w64(c2);
     const uint64_t m1 = __builtin_amdgcn_ballot_w64(c1);
-    w = add_twice_carry(w, mp);
-    w = add_twice_carry(w, ~(m4 ^ mp));
-    w = add_twice_carry(w, ~(m2 ^ mp));
-    return add_twice_carry(w, ~(m1 ^ mp));
+    w = add_twice_carry<true>(w, mp);
+    w = add_twice_carry<false>(w, ~(m4 ^ mp));
+    w = add_twice_carry<false>(w, ~(m2 ^ mp));
+    return add_twice_carry<false>(w, ~(m1 ^ mp));
 }
 
 // Encodes the vector whose 16-lane group holds x (lane g: dims 16 g ..); returns the fp32 norm and
