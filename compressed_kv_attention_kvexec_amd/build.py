@@ -25,8 +25,10 @@ SOURCES = ["tq4_api.cpp", "tq4_codebook.cpp", "tq4_encode.hip", "tq4_decode.hip"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-function"]
+# Kernel arguments that lead with scalars (pointers, sizes) are preloaded into scalar registers at
+# wave launch, so a kernel's first memory requests do not wait for a read of its argument block.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fno-gpu-rdc"]
+          "-fno-gpu-rdc", "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def _compile(src: str) -> str:

@@ -104,8 +104,15 @@ DecodePlan plan_decode(int32_t batch, int32_t max_seq_len, int32_t n_q_heads, in
 // the NB wavefronts of a slot read the same tiles (one HBM read, the others hit the caches) and
 // each keeps one block's 64 accumulators.  Decode is NB = 1, NS = 8 (two wavefronts per SIMD);
 // the multi-query verifier uses NB = 2 or 3 with NS = 4 (two or three per SIMD).
+//
+// The leading scalar arguments repeat what the first loads need (the pool, the page table and
+// its geometry): the library is built to preload them into scalar registers at wave launch, so
+// the page-ID and first-tile requests do not wait for a read of the argument block.
 template <int NB, int NS>
-__global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(
+    const uint32_t *k_words, const uint32_t *v_words, const uint16_t *k_norms, const uint16_t *v_norms,
+    const int32_t *page_table, int32_t table_stride, int32_t split_tiles, int32_t num_pages,
+    uint32_t page_size_nkv, DecodeArgs a) {
     constexpr int NW = NB * NS;
     constexpr int NT = NW * kWave;
     constexpr int NCOL = 16 * NB;
@@ -118,7 +125,16 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
     __shared__ float resL[NCOL];
     __shared__ int32_t progress[NW];  // tiles each wavefront has started
 
-    const DecodeParams &p = a.p;
+    DecodeParams p = a.p;
+    p.k_words = k_words;
+    p.v_words = v_words;
+    p.k_norms = k_norms;
+    p.v_norms = v_norms;
+    p.page_table = page_table;
+    p.table_stride = table_stride;
+    p.num_pages = num_pages;
+    p.page_size = static_cast<int32_t>(page_size_nkv & 0xffffu);
+    p.n_kv = static_cast<int32_t>(page_size_nkv >> 16);
     const int G = a.group;
     const int KQ = a.n_queries;
     const int ROWS = a.rows;  // KQ * G <= NCOL
@@ -126,10 +142,9 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
 
-    const int L_req = p.seq_lens[b];  // scalar load, requested first; used after the tile issue
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int slot = wave_u % NS, blk = wave_u / NS;
-    const int split_keys = a.split_tiles * kTile;
+    const int split_keys = split_tiles * kTile;
     const int key_begin = s * split_keys;
     const int32_t *pt_row = p.page_table + static_cast<int64_t>(b) * p.table_stride;
     const bool append_mode = p.k_new != nullptr || p.v_new != nullptr;
@@ -179,8 +194,10 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
     // tile, all before the length is known.  A first tile past the length is a real but unused
     // load of a valid record.  Every path issues exactly these loads in this order, so the
     // compiler's wait counts stay exact through the prologue.
+    fetch_pids(0);  // preloaded arguments only
+    __builtin_amdgcn_sched_barrier(0);
+    const int L_req = p.seq_lens[b];  // scalar load; used after the tile issue
     const u32x2 q_raw0 = *reinterpret_cast<const u32x2 *>(p.q + row_off(min(wave_u, ROWS - 1)) + 4 * lane);
-    fetch_pids(0);
     issue(slot, 0, true);
 
     const int L = L_req < 0 ? 0 : (L_req > p.max_seq_len ? p.max_seq_len : L_req);
@@ -524,9 +541,9 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(DecodeA
                 else
                     res4[quad_at(r0 + rr, qd)] = sum;
             }
+            if (n_active > 1 && r0 + kMergeRows >= ROWS) return;  // partial stored, no LDS reuse follows
             __syncthreads();
         }
-        if (n_active > 1) return;
     } else {
         // ---- merge the waves of each block.  Each lane rescales its accumulators (all of column
         // n) to the block's maximum over its waves (and back from 2^eo); then a fixed-order tree in
@@ -655,20 +672,24 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// The leading scalar arguments repeat what the first loads need, preloaded into scalar registers
+// at wave launch as in the split kernel.
 template <bool kRotated>
-__global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(const float *parts, const int32_t *seq_lens,
+                                                                          int32_t n_splits, int32_t partial_floats,
+                                                                          int32_t n_kv, CombineArgs a) {
     __shared__ float4v part[kCombWaves][kWave];
     const int G = a.group;
     const int r = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int L_req = a.seq_lens[b];
-    const size_t pf = static_cast<size_t>(a.partial_floats);
-    const float *base = a.parts + (static_cast<size_t>(b) * a.n_kv + g) * a.n_splits * pf;
+    const int L_req = seq_lens[b];
+    const size_t pf = static_cast<size_t>(partial_floats);
+    const float *base = parts + (static_cast<size_t>(b) * n_kv + g) * n_splits * pf;
     const float *mrow = base + r;
     const float *lrow = base + kSplitStatPad + r;
     const float *orow = base + 2 * kSplitStatPad + static_cast<size_t>(r) * kDim + 4 * lane;
-    const int ns = a.n_splits;
+    const int ns = n_splits;
     // Every load of the first group of 64 splits is issued before the length is known (slots past
     // the live splits hold stale data and are dropped by selection, never multiplied in).
     const int s_l = min(lane, ns - 1);
@@ -743,9 +764,11 @@ __global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(Combin
 hipError_t launch_split_combine(const CombineArgs &c, bool rotated, hipStream_t stream) {
     const dim3 grid(c.rows, c.n_kv, c.batch);
     if (rotated)
-        hipLaunchKernelGGL(tq4_decode_combine_kernel<true>, grid, dim3(kCombThreads), 0, stream, c);
+        hipLaunchKernelGGL(tq4_decode_combine_kernel<true>, grid, dim3(kCombThreads), 0, stream, c.parts, c.seq_lens,
+                           c.n_splits, c.partial_floats, c.n_kv, c);
     else
-        hipLaunchKernelGGL(tq4_decode_combine_kernel<false>, grid, dim3(kCombThreads), 0, stream, c);
+        hipLaunchKernelGGL(tq4_decode_combine_kernel<false>, grid, dim3(kCombThreads), 0, stream, c.parts, c.seq_lens,
+                           c.n_splits, c.partial_floats, c.n_kv, c);
     return hipGetLastError();
 }
 
@@ -762,19 +785,24 @@ hipError_t launch_decode(const DecodeParams &p, const DecodePlan &plan, hipStrea
     lut_pairs_from_codebook(a.lut_pairs, codebook().centroid);
     for (int i = 0; i < 15; ++i) a.thr[i] = codebook().threshold[i];
     const dim3 grid(plan.n_splits, p.n_kv, p.batch);
+    const uint32_t ps_nkv = static_cast<uint32_t>(p.page_size) | (static_cast<uint32_t>(p.n_kv) << 16);
+#define TQ4_SPLIT_ARGS                                                                                   \
+    p.k_words, p.v_words, p.k_norms, p.v_norms, p.page_table, p.table_stride, plan.split_tiles, p.num_pages, \
+        ps_nkv, a
     switch (plan.col_blocks) {
         case 1:
-            hipLaunchKernelGGL((tq4_attn_split_kernel<1, 8>), grid, dim3(8 * kWave), 0, stream, a);
+            hipLaunchKernelGGL((tq4_attn_split_kernel<1, 8>), grid, dim3(8 * kWave), 0, stream, TQ4_SPLIT_ARGS);
             break;
         case 2:
-            hipLaunchKernelGGL((tq4_attn_split_kernel<2, 4>), grid, dim3(8 * kWave), 0, stream, a);
+            hipLaunchKernelGGL((tq4_attn_split_kernel<2, 4>), grid, dim3(8 * kWave), 0, stream, TQ4_SPLIT_ARGS);
             break;
         case 3:
-            hipLaunchKernelGGL((tq4_attn_split_kernel<3, 4>), grid, dim3(12 * kWave), 0, stream, a);
+            hipLaunchKernelGGL((tq4_attn_split_kernel<3, 4>), grid, dim3(12 * kWave), 0, stream, TQ4_SPLIT_ARGS);
             break;
         default:
             return hipErrorInvalidValue;
     }
+#undef TQ4_SPLIT_ARGS
     if (plan.n_splits > 1) {
         CombineArgs c;
         c.parts = reinterpret_cast<const float *>(static_cast<const char *>(p.workspace) + plan.counters_bytes);
