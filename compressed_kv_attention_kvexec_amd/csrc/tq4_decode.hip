@@ -223,7 +223,7 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(
                       __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
         wave_fwht(y, lane);
         float mx = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
-        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+        mx = wave_max_f32(mx, lane);
         const int e = q_exponent(mx);
         const float qs = ldexpf(1.0f, e);
         if (lane == 0) row_f[r] = p.scale * 1.4426950408889634f * ldexpf(1.0f, -e) * (1.0f / 256.0f);
@@ -465,7 +465,9 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_attn_split_kernel(
     if constexpr (kPaired) __builtin_amdgcn_s_setprio(0);
 
     // ---- per-wave softmax totals (the statistics live outside the table, so they are written
-    // before the barrier that retires the table)
+    // before the barrier that retires the table).  These two exchanges go through the LDS
+    // crossbar: their lane-swap form needs two more registers here, where every accumulator is
+    // live, and spills in the three-block verifier.
     float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
     l_tot = ldexpf(l_tot + __shfl_xor(l_tot, 32, kWave), eo);  // true scale: relative to m_run
     if (gq == 0) {
@@ -660,18 +662,6 @@ constexpr int kCombWaves = 4;
 constexpr int kCombThreads = kCombWaves * kWave;
 constexpr int kCombPerWave = kWave / kCombWaves;  // splits per wavefront in each group of 64
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
 // The leading scalar arguments repeat what the first loads need, preloaded into scalar registers
 // at wave launch as in the split kernel.
 template <bool kRotated>
@@ -716,7 +706,7 @@ __global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(const 
         const int s = c * kWave + lane;
         if (s < n_active) mx = fmaxf(mx, mrow[s * pf]);
     }
-    const float M = wave_max(mx);
+    const float M = wave_max_f32(mx, lane);
 
     auto weight = [&](float m) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M); };
     float w_l = lane < n_active ? weight(m0) : 0.f;  // lane i: weight of split i
@@ -740,7 +730,7 @@ __global__ __launch_bounds__(kCombThreads) void tq4_decode_combine_kernel(const 
             }
         }
     }
-    const float Ltot = wave_sum(lsum);
+    const float Ltot = wave_sum_f32(lsum, lane);
     part[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && merge) {

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kValuThreads) void tq4_attn_valu_kernel(ValuArgs a)
         if constexpr (!kLiteral) {
             wave_fwht(y, lane);
             float mx = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
-            for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+            mx = wave_max_f32(mx, lane);
             const int e = q_exponent(mx);
             const float qs = ldexpf(1.0f, e);
 #pragma unroll

@@ -107,6 +107,25 @@ __device__ __forceinline__ float lane_xor(float x, int lane) {
     return __builtin_bit_cast(float, lane_xor<M>(__builtin_bit_cast(uint32_t, x), lane));
 }
 
+// Maximum and sum of x over the whole wavefront, in every lane: partners lane ^ 32, ^ 16, ..., ^ 1
+// in that order (the sum pairs the same values as a butterfly over __shfl_xor would).
+__device__ __forceinline__ float wave_max_f32(float x, int lane) {
+    x = fmaxf(x, lane_xor<32>(x, lane));
+    x = fmaxf(x, lane_xor<16>(x, lane));
+    x = fmaxf(x, lane_xor<8>(x, lane));
+    x = fmaxf(x, lane_xor<4>(x, lane));
+    x = fmaxf(x, lane_xor<2>(x, lane));
+    return fmaxf(x, lane_xor<1>(x, lane));
+}
+__device__ __forceinline__ float wave_sum_f32(float x, int lane) {
+    x += lane_xor<32>(x, lane);
+    x += lane_xor<16>(x, lane);
+    x += lane_xor<8>(x, lane);
+    x += lane_xor<4>(x, lane);
+    x += lane_xor<2>(x, lane);
+    return x + lane_xor<1>(x, lane);
+}
+
 // For M = 16 or 32: the pair (lo, hi) with lo = the value of the lower lane of each (l, l ^ M)
 // pair and hi = the value of the upper lane, in every lane (one swap instruction, no select).
 template <int M>

@@ -51,9 +51,7 @@ struct Int8EncodeArgs {
 
 __device__ __forceinline__ float wave_max_abs(const float x[4]) {
     float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, kWave));
-    return m;
+    return wave_max_f32(m, static_cast<int>(threadIdx.x) & (kWave - 1));
 }
 
 // One code: clamp(rint(x / s), -127, 127) as a byte (s > 0), correctly rounded division.
@@ -548,8 +546,8 @@ __global__ __launch_bounds__(NB * NS * kWave) void tq4_int8_split_kernel(Int8Dec
 
     // ---- merge the wavefronts of each block: rescale to the block maximum, then a fixed-order
     // tree in LDS, kTreeBlocks blocks at a time (only query-row lanes take part)
-    float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-    l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
+    float l_tot = l_run + lane_xor<16>(l_run, lane);
+    l_tot = l_tot + lane_xor<32>(l_tot, lane);
     if (gq == 0) {
         stat_m[wave_u][n] = m_run;
         stat_l[wave_u][n] = l_tot;
@@ -962,8 +960,8 @@ void tq4_int8_prefill_kernel(Int8PrefillArgs a) {
     }
 
     // ---- partial: lane (gq, n) holds row n, dims 16 (4 gq + r) + e in oacc[e][r]
-    float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-    l_tot = l_tot + __shfl_xor(l_tot, 32, kWave);
+    float l_tot = l_run + lane_xor<16>(l_run, lane);
+    l_tot = l_tot + lane_xor<32>(l_tot, lane);
     if (!live) return;
     float *dst = reinterpret_cast<float *>(ws + a.parts_off) +
                  ((static_cast<int64_t>(g) * a.rows + row) * a.n_splits + s) * kPfPartial;

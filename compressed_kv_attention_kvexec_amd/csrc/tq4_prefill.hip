@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void tq4_prefill_rotate_kernel(PrefillArgs a) 
                   __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
     wave_fwht(y, lane);
     float mx = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, kWave));
+    mx = wave_max_f32(mx, lane);
     const int e = q_exponent(mx);
     const float qs = ldexpf(1.0f, e);
     char *ws = static_cast<char *>(p.workspace);
@@ -527,8 +527,8 @@ void tq4_prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int row = row0 + 16 * j + n;
-        float l_tot = l_run[j] + __shfl_xor(l_run[j], 16, kWave);
-        l_tot = (l_tot + __shfl_xor(l_tot, 32, kWave)) * escale;
+        float l_tot = l_run[j] + lane_xor<16>(l_run[j], lane);
+        l_tot = (l_tot + lane_xor<32>(l_tot, lane)) * escale;
         if (row >= a.rows) continue;
         float *dst = parts + ((static_cast<int64_t>(g) * a.rows + row) * a.n_splits + s) * kPfPartial;
 #pragma unroll

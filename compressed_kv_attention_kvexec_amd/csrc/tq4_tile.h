@@ -128,6 +128,24 @@ __device__ __forceinline__ void load_v(const Pool &p, int64_t rec0, const LaneOf
     for (int h = 0; h < 2; ++h) t.vn[h] = *reinterpret_cast<const u32x2 *>(nb + o.nrm + 32u * h);
 }
 
+// One stage h = 4 M of wave_fwht below: lane l pairs with lane l ^ M (DPP moves or the
+// lane-swap instructions, no LDS crossbar); the lower lane keeps a + b, the upper a - b.
+template <int M>
+__device__ __forceinline__ void wave_fwht_stage(float y[4], int lane) {
+    const bool upper = (lane & M) != 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if constexpr (M >= 16) {
+            float lo, hi;
+            lane_pair<M>(y[r], lo, hi);
+            y[r] = upper ? (lo - hi) : (lo + hi);
+        } else {
+            const float o = lane_xor<M>(y[r], lane);
+            y[r] = upper ? (o - y[r]) : (y[r] + o);
+        }
+    }
+}
+
 // Unnormalised Hadamard transform of one 256-vector held by a wavefront, lane l holding dims
 // 4l .. 4l+3: stages 1 and 2 in registers, stages 4 .. 128 pair lane l with lane l ^ (h / 4).
 __device__ __forceinline__ void wave_fwht(float y[4], int lane) {
@@ -138,15 +156,12 @@ __device__ __forceinline__ void wave_fwht(float y[4], int lane) {
         y[1] = t1 + t3;
         y[3] = t1 - t3;
     }
-#pragma unroll
-    for (int m = 1; m <= 32; m <<= 1) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float o = __shfl_xor(y[r], m, kWave);
-            y[r] = upper ? (o - y[r]) : (y[r] + o);
-        }
-    }
+    wave_fwht_stage<1>(y, lane);
+    wave_fwht_stage<2>(y, lane);
+    wave_fwht_stage<4>(y, lane);
+    wave_fwht_stage<8>(y, lane);
+    wave_fwht_stage<16>(y, lane);
+    wave_fwht_stage<32>(y, lane);
 }
 
 
