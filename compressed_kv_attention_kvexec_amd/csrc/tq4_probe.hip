@@ -1,5 +1,10 @@
-// tq4_probe.hip -- streaming-read bandwidth probe (tq4_probe.h): a plain grid-stride read
-// with four 16-byte loads in flight per thread, 256 threads per workgroup.
+// tq4_probe.hip -- streaming-read bandwidth probe (tq4_probe.h).
+//
+// The buffer is cut into blocks of kProbeThreads * U 16-byte words; workgroup w reads blocks
+// w, w + W, w + 2 W, ... (W workgroups).  Inside a block, thread t loads words t + kProbeThreads k
+// for k < U, all U loads issued before any is used, so every load instruction of a wavefront covers
+// one contiguous KiB and a workgroup has kProbeThreads * U * 16 bytes in flight.  The loaded words
+// are folded with XOR into one word per thread, so no load can be dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,25 +13,29 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kProbeThreads = 256;
+constexpr int kProbeThreads = 512;
 
-__global__ __launch_bounds__(kProbeThreads) void tq4_probe_read_kernel(const u32x4 *p, size_t n64, uint32_t *sink) {
-    // thread t reads 16-byte words t, t + S, t + 2 S, ... (S = threads in the grid), four per
-    // iteration, so each load instruction of a wavefront covers one contiguous KiB
-    const size_t stride = static_cast<size_t>(gridDim.x) * kProbeThreads;
-    const size_t tid = static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
-    const size_t n = n64 * 4;  // 16-byte words
+template <int U>
+__global__ __launch_bounds__(kProbeThreads) void tq4_probe_read_kernel(const u32x4 *p, size_t n16, uint32_t *sink) {
+    constexpr size_t kBlock = static_cast<size_t>(kProbeThreads) * U;  // 16-byte words per block
+    const size_t n_full = n16 / kBlock;
+    const size_t t = threadIdx.x;
     uint32_t acc = 0;
-    size_t i = tid;
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        const u32x4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    for (size_t blk = blockIdx.x; blk < n_full; blk += gridDim.x) {
+        const u32x4 *b = p + blk * kBlock + t;
+        u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) v[k] = b[static_cast<size_t>(k) * kProbeThreads];
+#pragma unroll
+        for (int k = 0; k < U; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
     }
-    for (; i < n; i += stride) {
+    // the words past the last full block, one load per thread and step
+    const size_t stride = static_cast<size_t>(gridDim.x) * kProbeThreads;
+    for (size_t i = n_full * kBlock + static_cast<size_t>(blockIdx.x) * kProbeThreads + t; i < n16; i += stride) {
         const u32x4 a = p[i];
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
-    sink[tid] = acc;
+    sink[static_cast<size_t>(blockIdx.x) * kProbeThreads + t] = acc;
 }
 
 }  // namespace
@@ -38,13 +47,21 @@ size_t tq4_probe_sink_words(int32_t workgroups) {
     return static_cast<size_t>(workgroups) * kProbeThreads;
 }
 
-int tq4_probe_stream_read(const void *src, size_t bytes, void *sink, int32_t workgroups, void *stream) {
-    if (src == nullptr || sink == nullptr || bytes == 0 || bytes % 64 != 0) return -1;
+int tq4_probe_stream_read(const void *src, size_t bytes, void *sink, int32_t workgroups, int32_t loads_in_flight,
+                          void *stream) {
+    if (src == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0) return -1;
     if ((reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3) != 0) return -1;
     if (workgroups < 1 || workgroups > 65535) return -1;
-    hipLaunchKernelGGL(tq4_probe_read_kernel, dim3(static_cast<unsigned>(workgroups)), dim3(kProbeThreads), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src), bytes / 64,
-                       static_cast<uint32_t *>(sink));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4 *p = static_cast<const u32x4 *>(src);
+    uint32_t *out = static_cast<uint32_t *>(sink);
+    const dim3 grid(static_cast<unsigned>(workgroups)), block(kProbeThreads);
+    switch (loads_in_flight) {
+        case 4: hipLaunchKernelGGL(tq4_probe_read_kernel<4>, grid, block, 0, s, p, bytes / 16, out); break;
+        case 8: hipLaunchKernelGGL(tq4_probe_read_kernel<8>, grid, block, 0, s, p, bytes / 16, out); break;
+        case 16: hipLaunchKernelGGL(tq4_probe_read_kernel<16>, grid, block, 0, s, p, bytes / 16, out); break;
+        default: return -1;
+    }
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
