@@ -478,10 +478,11 @@ def torch_sum_read(device, gib: int = 4, reps: int = 5) -> float:
     return best
 
 
-def stream_read_probe(device, gib: int = 4, reps: int = 5) -> dict:
+def stream_read_probe(device, gib: int = 4, reps: int = 5, call_bytes: int = 0) -> dict:
     """Read rate of the streaming-read probe (libtq4probe.so, compressed_kv_attention_kvexec_amd/csrc/tq4_probe.h)
     over `gib` GiB: the best over grid sizes, loads in flight per thread and `reps` repetitions,
-    i.e. what a plain streaming-read kernel reaches on this device."""
+    i.e. what a plain streaming-read kernel reaches on this device; with call_bytes, also the best
+    configuration's cold time over that many bytes."""
     import ctypes
     import torch
     from compressed_kv_attention_kvexec_amd import build as hipbuild
@@ -514,11 +515,33 @@ def stream_read_probe(device, gib: int = 4, reps: int = 5) -> dict:
             if top > best["gb_per_s"]:
                 best = {"gb_per_s": top, "workgroups": wgs, "loads_in_flight": u}
             del sink
-    del x
-    torch.cuda.empty_cache()
     best["bytes"] = nbytes
     best["threads_per_workgroup"] = 512
     best["sweep"] = sweep
+    if call_bytes:
+        # the best configuration over one decode call's byte count, timed like the one-layer decode
+        # legs (768 MiB read before every call): a plain read's time for those bytes, launch included
+        nb = call_bytes // 16 * 16
+        sink = torch.empty(lib.tq4_probe_sink_words(best["workgroups"]), dtype=torch.int32, device=device)
+        args = (ctypes.c_void_p(x.data_ptr()), nb, ctypes.c_void_p(sink.data_ptr()), best["workgroups"],
+                best["loads_in_flight"], stream)
+        flush = torch.ones(192 << 20, dtype=torch.float32, device=device)
+        times = []
+        for i in range(23):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.tq4_probe_stream_read(*args)
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        t = sorted(times)[len(times) // 2]
+        best["call_bytes"] = {"bytes": nb, "us": t, "gb_per_s": nb / t / 1e3,
+                              "timing": "median of 20 cold reads (768 MiB read before each)"}
+        del flush, sink
+    del x
+    torch.cuda.empty_cache()
     return best
 
 
@@ -920,11 +943,15 @@ def main() -> int:
     del layers
     torch.cuda.empty_cache()
     if not args.no_probe:
-        # reference points for plain streaming reads over 4 GiB (not ceilings of this kernel)
+        # plain streaming reads over 4 GiB: torch's reduction and the probe's sweep (a measured ceiling)
         result["extra"]["torch_sum_read_gb_per_s"] = torch_sum_read(dev)
-        result["extra"]["stream_read_probe"] = stream_read_probe(dev)
+        probe = result["extra"]["stream_read_probe"] = stream_read_probe(dev, call_bytes=head["bytes_per_launch"])
+        # the decode call's rate as a fraction of the best plain streaming read measured here
+        result["extra"]["decode_frac_of_stream_read_probe"] = result["roofline"]["achieved"] / probe["gb_per_s"]
         log(f"torch.sum over 4 GiB fp32: {result['extra']['torch_sum_read_gb_per_s']:.0f} GB/s; stream-read probe "
-            f"{result['extra']['stream_read_probe']['gb_per_s']:.0f} GB/s")
+            f"{probe['gb_per_s']:.0f} GB/s ({probe['loads_in_flight']} loads in flight, {probe['workgroups']} "
+            f"workgroups); decode call at {result['extra']['decode_frac_of_stream_read_probe']:.3f} of it; "
+            f"the probe over one call's {probe['call_bytes']['bytes'] / 1e6:.1f} MB: {probe['call_bytes']['us']:.1f} us cold")
     configs = result["extra"]["configs"] = {}
     if not args.no_configs:
         for name in ("decode_1k_p64", "decode_32k"):
