@@ -862,6 +862,8 @@ def main() -> int:
     ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth reference points")
     ap.add_argument("--only-config", default="",
                     help="run only the cold one-layer timing of this decode workload (profiler runs)")
+    ap.add_argument("--queries", type=int, default=1,
+                    help="with --only-config: time the packed verifier with this many query tokens per request")
     ap.add_argument("--only-step", default="",
                     help="run only the timed decode step of this workload, no other leg (profiler runs)")
     ap.add_argument("--only-prefill", action="store_true",
@@ -892,7 +894,8 @@ def main() -> int:
         if args.calibrate_copy_mib > 0:
             calibration_copy(args.calibrate_copy_mib, dev)
         variants = tuple(v for v in args.variants.split(",") if v)
-        print(json.dumps({"decode_config": decode_config_leg(args.only_config, dev, variants=variants)}), flush=True)
+        print(json.dumps({"decode_config": decode_config_leg(args.only_config, dev, n_queries=args.queries,
+                                                             variants=variants)}), flush=True)
         return 0
     if args.int8_only:  # the INT8 arm alone, for profiler runs
         if args.calibrate_copy_mib > 0:
