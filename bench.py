@@ -123,8 +123,8 @@ def build_layers(w, device, stats=None):
 
 def encode_leg(layer, w, device, tokens: int = 32768, reps: int = 10, groups: int = 5):
     """Encode throughput: back-to-back launches writing K and V of `tokens` tokens into layer 0's
-    pool (its first used slots, rewritten with the same records), timed with events; the median
-    over `groups` groups of `reps` launches."""
+    pool (its first used slots, rewritten with the same records), timed with events after 200
+    untimed launches; the median over `groups` groups of `reps` launches."""
     import numpy as np
     import torch
     import compressed_kv_attention_kvexec_amd as tq4
@@ -133,7 +133,9 @@ def encode_leg(layer, w, device, tokens: int = 32768, reps: int = 10, groups: in
     k = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_K), (tokens, w.n_kv, 256), device)
     v = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_V), (tokens, w.n_kv, 256), device)
     call = tq4.prepare_encode(layer["pool"], k, v, slots)
-    for _ in range(3):
+    # ~15 ms of untimed launches first: the encoder is bound by vector-ALU issue, so its rate
+    # follows the compute clock, which settles only after some milliseconds of load
+    for _ in range(200):
         call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     times = []
