@@ -133,8 +133,8 @@ def encode_leg(layer, w, device, tokens: int = 32768, reps: int = 10, groups: in
     k = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_K), (tokens, w.n_kv, 256), device)
     v = synth.torch_normal(synth.seed_of(w.wid, 0, synth.T_V), (tokens, w.n_kv, 256), device)
     call = tq4.prepare_encode(layer["pool"], k, v, slots)
-    # ~15 ms of untimed launches first: the encoder is bound by vector-ALU issue, so its rate
-    # follows the compute clock, which settles only after some milliseconds of load
+    # ~15 ms of untimed launches first: the first milliseconds of launches run slower (a median of
+    # 72 us over the first 200 against 63 us afterwards in a profiled run)
     for _ in range(200):
         call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
